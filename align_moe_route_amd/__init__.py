@@ -1,0 +1,202 @@
+"""Python binding of libmoe_route_sort.so: argument marshalling only.
+
+Every step of the route-sort path (FP32 conversion, bias, grouped top-k,
+histogram, prefix, scatter) runs in the HIP kernels behind the C ABI declared
+in include/moe_route_sort.h.  This module checks tensors, allocates outputs
+when the caller gives none, and forwards raw device pointers and the current
+HIP stream.  It fails loudly when the library is not built; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_route_sort.so")
+
+MRS_OK = 0
+MRS_ERR_INVALID_ARG = -1
+MRS_ERR_NULL_POINTER = -2
+MRS_ERR_MISALIGNED = -3
+MRS_ERR_WORKSPACE = -4
+MRS_ERR_OVERFLOW = -5
+MRS_ERR_LAUNCH = -6
+MRS_DTYPE_F32 = 0
+MRS_DTYPE_BF16 = 1
+FLAG_FORCE_SINGLE_WG = 1
+FLAG_FORCE_MULTI_WG = 2
+FLAG_FORCE_EXACT = 4
+
+EXPORTED = [
+    "moe_route_sort",
+    "moe_route_sort_ex",
+    "moe_route_sort_max_rows",
+    "moe_route_sort_max_blocks",
+    "moe_route_sort_workspace_bytes",
+    "moe_route_sort_strerror",
+    "moe_route_sort_sigmoid_probe",
+]
+
+_lib = None
+
+
+class RouteSortError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"moe_route_sort failed ({code}): {strerror(code)}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python align_moe_route_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    common = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.moe_route_sort.argtypes = common
+    L.moe_route_sort.restype = i32
+    L.moe_route_sort_ex.argtypes = common + [ctypes.c_uint, vp]
+    L.moe_route_sort_ex.restype = i32
+    for name in ("moe_route_sort_max_rows", "moe_route_sort_max_blocks"):
+        getattr(L, name).argtypes = [i32, i32, i32, i32]
+        getattr(L, name).restype = ctypes.c_int64
+    L.moe_route_sort_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.moe_route_sort_workspace_bytes.restype = sz
+    L.moe_route_sort_strerror.argtypes = [i32]
+    L.moe_route_sort_strerror.restype = ctypes.c_char_p
+    L.moe_route_sort_sigmoid_probe.argtypes = [vp, i32, vp, vp, vp]
+    L.moe_route_sort_sigmoid_probe.restype = i32
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().moe_route_sort_strerror(int(code)).decode()
+
+
+def max_rows(M: int, E: int, k: int, block: int) -> int:
+    return int(lib().moe_route_sort_max_rows(M, E, k, block))
+
+
+def max_blocks(M: int, E: int, k: int, block: int) -> int:
+    return int(lib().moe_route_sort_max_blocks(M, E, k, block))
+
+
+def workspace_bytes(M: int, E: int, k: int, block: int) -> int:
+    v = int(lib().moe_route_sort_workspace_bytes(M, E, k, block))
+    if v == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    return v
+
+
+def raw_call(logits_ptr, bias_ptr, M, E, k, n_group, topk_group, block, out_ids_ptr, out_w_ptr,
+             sorted_ids_ptr, eob_ptr, npp_ptr, dtype, ws_ptr, ws_bytes, stream_ptr,
+             flags: int = 0, stats_ptr=None) -> int:
+    """Direct C-ABI call with integer device pointers; returns the MRS code."""
+    return int(lib().moe_route_sort_ex(logits_ptr, bias_ptr, M, E, k, n_group, topk_group, block,
+                                       out_ids_ptr, out_w_ptr, sorted_ids_ptr, eob_ptr, npp_ptr,
+                                       dtype, ws_ptr, ws_bytes, stream_ptr, flags, stats_ptr))
+
+
+class RouteSortOutput(NamedTuple):
+    ids: "torch.Tensor"              # [M, k] int32, ascending expert ids per token
+    weights: "torch.Tensor"          # [M, k] float32
+    sorted_ids: "torch.Tensor"       # [max_rows] int32; [0, num_post_pad) defined
+    expert_of_block: "torch.Tensor"  # [max_blocks] int32; [0, num_post_pad/block) defined
+    num_post_pad: "torch.Tensor"     # [1] int32 (device)
+
+
+_ws_cache = {}
+
+
+def _workspace(device, nbytes: int):
+    import torch
+    key = (str(device), nbytes)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
+               out: Optional[RouteSortOutput] = None, workspace=None, flags: int = 0,
+               stats=None, stream=None) -> RouteSortOutput:
+    """Run the route-sort path on the GPU.
+
+    logits: [M, E] float32 or bfloat16 CUDA/HIP tensor, contiguous.
+    bias:   [E] float32 tensor on the same device.
+    out:    optional preallocated RouteSortOutput (reused, nothing else written).
+    workspace: optional uint8 tensor of at least workspace_bytes() bytes that
+            was zeroed once; by default a cached per-device buffer is used.
+    stats:  optional int32 [2] device tensor (exact-path / fast-path token counts).
+    """
+    import torch
+    if not (isinstance(logits, torch.Tensor) and logits.is_cuda):
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [M, E] tensor")
+    if logits.dtype == torch.float32:
+        dt = MRS_DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = MRS_DTYPE_BF16
+    else:
+        raise NotImplementedError(f"logits dtype {logits.dtype} (float32 or bfloat16 only)")
+    M, E = logits.shape
+    if not (isinstance(bias, torch.Tensor) and bias.device == logits.device and
+            bias.dtype == torch.float32 and bias.shape == (E,) and bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [E] tensor on the logits' device")
+    dev = logits.device
+    rows = max_rows(M, E, k, block)
+    blocks = max_blocks(M, E, k, block)
+    if rows < 0:
+        raise ValueError("invalid sizes or row capacity overflow")
+    if out is None:
+        out = RouteSortOutput(
+            torch.empty((M, k), dtype=torch.int32, device=dev),
+            torch.empty((M, k), dtype=torch.float32, device=dev),
+            torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
+            torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
+            torch.empty((1,), dtype=torch.int32, device=dev),
+        )
+    else:
+        for t, dtype, shape in ((out.ids, torch.int32, (M, k)), (out.weights, torch.float32, (M, k))):
+            if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+                raise ValueError("out.ids / out.weights have the wrong dtype, shape or device")
+        if (out.sorted_ids.numel() < rows or out.expert_of_block.numel() < blocks or
+                out.sorted_ids.dtype != torch.int32 or out.expert_of_block.dtype != torch.int32 or
+                out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
+            raise ValueError("out metadata buffers too small or of the wrong dtype")
+    nbytes = workspace_bytes(M, E, k, block)
+    if workspace is None:
+        workspace = _workspace(dev, nbytes) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = raw_call(logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block,
+                  out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
+                  out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt, ws_ptr, ws_len,
+                  stream.cuda_stream, flags, stats.data_ptr() if stats is not None else None)
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return out
+
+
+def sigmoid_probe(x):
+    """Both sigmoid forms of the kernels on a float32 GPU tensor (diagnostics)."""
+    import torch
+    x = x.contiguous()
+    f = torch.empty_like(x)
+    e = torch.empty_like(x)
+    rc = lib().moe_route_sort_sigmoid_probe(x.data_ptr(), x.numel(), f.data_ptr(), e.data_ptr(),
+                                            torch.cuda.current_stream(x.device).cuda_stream)
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return f, e

@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Route-sort benchmark on one MI355X.
+
+One step = one complete route-sort call (FP32 conversion, correction bias,
+grouped top-k, per-expert histogram, padded exclusive prefix, stable scatter,
+expert per block) over one batch of seeded synthetic router logits already
+resident in HBM.  The headline workload is the skewed prefill chunk (M=8192
+tokens, E=896 experts, top-16, 8 groups keep 4, block 128, BF16 logits with
+log-Zipf expert popularity).  To keep the logits out of the 256 MB last-level
+cache the timed loop rotates over distinct copies of the input totalling at
+least --rotate-mb megabytes.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import os
+
+os.environ.setdefault("OMP_NUM_THREADS", "1")        # the CPU oracle leg uses one core
+os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+os.environ.setdefault("MKL_NUM_THREADS", "1")
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import math  # noqa: E402
+import platform  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "routes/sec (M*k) + achieved HBM GB/s at M=8192; µs/call at M=1, E=896, k=16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, npp):
+    sz = 2 if cfg.dtype == "bf16" else 4
+    return (cfg.M * cfg.E * sz + 4 * cfg.E + 8 * cfg.M * cfg.k + 4 * npp + 4 * (npp // cfg.block) + 4)
+
+
+def to_gpu(inp, torch):
+    if inp.cfg.dtype == "bf16":
+        x = torch.from_numpy(inp.logits_storage.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x = torch.from_numpy(inp.logits_storage).cuda()
+    return x, torch.from_numpy(inp.bias).cuda()
+
+
+def time_workload(cfg, steps, warmup, rotate_mb, torch, amr):
+    inp = workloads.make_inputs(cfg)
+    x0, b = to_gpu(inp, torch)
+    mb = x0.numel() * x0.element_size() / 1e6
+    nrot = max(1, int(math.ceil(rotate_mb / mb))) if rotate_mb > 0 else 1
+    # distinct buffers with the same rows in a rotated order: same distribution,
+    # no reuse of cached lines between consecutive steps
+    xs = [x0] + [torch.roll(x0, shifts=(i * 997) % max(cfg.M, 1), dims=0).contiguous()
+                 for i in range(1, nrot)]
+    out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    npp = int(out.num_post_pad.item())
+    # host wall time per call, launch + synchronise (latency view)
+    t = time.perf_counter()
+    reps = min(steps, 50)
+    for i in range(reps):
+        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+        torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t) / reps * 1e6
+    nbytes = algorithmic_bytes(cfg, npp)
+    return dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
+                routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(cfg, budget_s=12.0, chunk=1024):
+    """The oracle as it stands, on the first tokens of the same workload, one
+    oracle call per chunk of tokens, until the time budget is spent."""
+    from oracle import route_sort as orc
+    inp = workloads.make_inputs(cfg)
+    done, spent = 0, 0.0
+    while done < cfg.M and spent < budget_s:
+        rows = np.arange(done, min(cfg.M, done + chunk))
+        t = time.perf_counter()
+        orc.route_sort(inp.logits_storage, cfg.dtype, inp.bias, cfg.k, cfg.n_group,
+                       cfg.topk_group, cfg.block, tokens=rows)
+        spent += time.perf_counter() - t
+        done += rows.size
+    return dict(value=done * cfg.k / spent, unit="routes/s", cores=1, kind="oracle",
+                sample=f"first {done} of {cfg.M} tokens of {cfg.name} (oracle route_sort per "
+                       f"{chunk}-token chunk: selection + sort metadata), {spent:.1f} s on one "
+                       f"core of {platform.processor() or platform.machine()}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill_skew", choices=list(workloads.CONFIGS))
+    ap.add_argument("--rotate-mb", type=float, default=600.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the route-sort path has no cross-GPU step "
+              "(each rank routes its own tokens); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import align_moe_route_amd as amr
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    amr.lib()
+
+    cfg = workloads.CONFIGS[args.workload]
+    log(f"[bench] {cfg.name}: M={cfg.M} E={cfg.E} k={cfg.k} steps={args.steps} warmup={args.warmup}")
+    torch.cuda.synchronize()
+    r = time_workload(cfg, args.steps, args.warmup, args.rotate_mb, torch, amr)
+    log(f"[bench] {cfg.name}: {r['ms']*1e3:.2f} us/call, {r['routes_per_s']:.3e} routes/s, "
+        f"{r['gbps']:.1f} GB/s algorithmic, {r['rot']} rotating input copies")
+
+    extra = {}
+    if not args.no_extra:
+        for name in workloads.CONFIG_ORDER:
+            if name == cfg.name:
+                continue
+            c = workloads.CONFIGS[name]
+            e = time_workload(c, max(20, args.steps // 4), 5, args.rotate_mb, torch, amr)
+            extra[name] = dict(us_per_call=round(e["ms"] * 1e3, 3),
+                               host_wall_us_per_call=round(e["wall_us"], 2),
+                               routes_per_s=e["routes_per_s"], algorithmic_gbps=round(e["gbps"], 1),
+                               frac_hbm_peak=round(e["gbps"] / HBM_PEAK_GBPS, 4))
+            log(f"[bench] {name}: {e['ms']*1e3:.2f} us/call, {e['routes_per_s']:.3e} routes/s, "
+                f"{e['gbps']:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg)
+        log(f"[bench] oracle: {cpu['value']:.3e} routes/s")
+
+    res = {
+        "metric": METRIC,
+        "value": r["routes_per_s"],
+        "unit": "routes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; BF16 logits N(0,1) + log-Zipf(1.1) expert offsets, bias U(-0.1,0.1))",
+        "config": {"workload": cfg.name, "M": cfg.M, "E": cfg.E, "k": cfg.k, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "block": cfg.block, "logits": cfg.dtype},
+        "hbm_gbps_algorithmic": r["gbps"],
+        "us_per_call": r["ms"] * 1e3,
+        "decode_us_per_call": extra.get("decode", {}).get("us_per_call"),
+        "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_call": r["nbytes"], "scope": "whole call"},
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * moe_route_sort.h -- C ABI of the MI355X (gfx950) MoE route-sort library.
+ *
+ * The operation (page "Kimi-K3 B1 route-sort + prepared-MoE handoff (stack)",
+ * Summary section): router logits are converted to FP32, a per-expert
+ * correction bias is added, a grouped top-k picks k experts per token, and the
+ * two sort phases turn the picks into expert-sorted, block-padded dispatch
+ * metadata that a grouped GEMM consumes directly, with no second top-k or sort.
+ *
+ * Definitions used by every entry point (t = token, j = pick, e = expert):
+ *   s[t,e]    = sigmoid(FP32(logits[t,e])), correctly rounded to FP32
+ *   key[t,e]  = FP32(s[t,e] + bias[e])              (choice uses the biased key)
+ *   groups    = n_group contiguous blocks of E / n_group experts; a group's
+ *               score is the FP32 sum of its two largest keys (its only key
+ *               when a group holds one expert); the topk_group best groups are
+ *               kept, ties to the lower group index
+ *   out_ids   = the k best keys inside the kept groups, ties to the lower
+ *               expert index, listed in ascending expert id
+ *   out_w     = s[t,id] / sum of s over the k picks (unbiased scores)
+ *   slot      = t*k + j; sentinel = M*k
+ *   count[e]  = number of slots routed to e (phase 1: histogram)
+ *   padded[e] = ceil(count[e] / block) * block
+ *   off[e]    = sum of padded[e'] for e' < e (phase 2: exclusive prefix)
+ *   sorted_ids[off[e] + r] = r-th slot routed to e in ascending slot order for
+ *               r < count[e]; sentinel for count[e] <= r < padded[e]
+ *   expert_of_block[b] = e for off[e] <= b*block < off[e] + padded[e]
+ *   *num_post_pad = sum of padded[e]
+ * The page "gfx1250 ordinary-TP route optimization" (Capacity and dispatch)
+ * bounds the expert set at 4096 (a 16 KiB histogram of 256-bucket tiles);
+ * this library keeps that bound.
+ *
+ * Memory: every pointer argument of moe_route_sort / moe_route_sort_ex is
+ * device memory owned by the caller.  Inputs are never written.  Nothing
+ * outside the defined ranges of the outputs is written.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL = the default stream), never
+ * synchronise the host, never allocate, and may be captured in a HIP graph.
+ *
+ * Errors: a negative return code, detected before any launch; on error the
+ * outputs are untouched.  moe_route_sort_strerror() names each code.
+ */
+#ifndef MOE_ROUTE_SORT_H
+#define MOE_ROUTE_SORT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MRS_OK = 0,
+  MRS_ERR_INVALID_ARG = -1,   /* a size or mode outside the contract below      */
+  MRS_ERR_NULL_POINTER = -2,  /* a required pointer is NULL                     */
+  MRS_ERR_MISALIGNED = -3,    /* logits not 16-byte aligned, or another array   */
+                              /* not 4-byte aligned                             */
+  MRS_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required     */
+  MRS_ERR_OVERFLOW = -5,      /* M*k or the row capacity does not fit int32     */
+  MRS_ERR_LAUNCH = -6         /* the HIP runtime rejected a kernel launch       */
+};
+
+enum { MRS_DTYPE_F32 = 0, MRS_DTYPE_BF16 = 1 };
+
+/*
+ * moe_route_sort -- the whole route-sort path in one call.
+ *
+ *   logits          [M, E] row-major, FP32 or BF16 (logits_dtype), 16-byte
+ *                   aligned base address.
+ *   bias            [E] FP32 correction bias.
+ *   M               tokens, M >= 0.  M == 0 writes *num_post_pad = 0 only.
+ *   E               experts, 1 <= E <= 4096.
+ *   k               picks per token, 1 <= k <= 64 and k <= topk_group * E / n_group.
+ *   n_group         groups, n_group >= 1 and E % n_group == 0.
+ *   topk_group      kept groups, 1 <= topk_group <= n_group.
+ *   block           padding granularity of each expert's segment, block >= 1.
+ *   out_ids         [M, k] int32 (written).
+ *   out_w           [M, k] FP32 (written).
+ *   sorted_ids      int32 of at least moe_route_sort_max_rows(M, E, k, block)
+ *                   entries; entries [0, *num_post_pad) are written.
+ *   expert_of_block int32 of at least moe_route_sort_max_blocks(M, E, k, block)
+ *                   entries; entries [0, *num_post_pad / block) are written.
+ *   num_post_pad    one int32 (written).
+ *   logits_dtype    MRS_DTYPE_F32 or MRS_DTYPE_BF16.
+ *   workspace       device scratch of at least moe_route_sort_workspace_bytes()
+ *                   bytes (may be NULL when that size is 0).  Zero it once when
+ *                   it is allocated; every call leaves it reusable, with no
+ *                   clearing between calls.  Calls that may overlap in time
+ *                   need distinct workspaces.
+ *   stream          hipStream_t cast to void* (NULL: default stream).
+ * Returns MRS_OK or a negative MRS_ERR_* code.
+ */
+int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                   int topk_group, int block, int32_t* out_ids, float* out_w,
+                   int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                   int logits_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Option bits for moe_route_sort_ex (path selection for tests and tuning;
+ * every path computes the same result). */
+enum {
+  MRS_FLAG_FORCE_SINGLE_WG = 1u << 0, /* one workgroup does everything (M*k <= 2048, M <= 64) */
+  MRS_FLAG_FORCE_MULTI_WG = 1u << 1,  /* many workgroups, even for small M                  */
+  MRS_FLAG_FORCE_EXACT = 1u << 2      /* skip the fast certified selection; every token     */
+                                      /* takes the exact workgroup-wide selection           */
+};
+
+/*
+ * moe_route_sort_ex -- moe_route_sort with option bits and optional device
+ * statistics.  `stats`, when not NULL, is device int32[2] that the call
+ * increments: stats[0] += tokens that took the exact workgroup-wide selection,
+ * stats[1] += tokens selected by the fast certified path.  Unknown flag bits
+ * or a forced path that cannot take the shape return MRS_ERR_INVALID_ARG.
+ */
+int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                      int topk_group, int block, int32_t* out_ids, float* out_w,
+                      int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                      int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      unsigned flags, int32_t* stats);
+
+/* Capacity of sorted_ids: M*k + min(E, M*k)*(block-1), or -1 when the
+ * arguments are invalid or the result does not fit int32. */
+int64_t moe_route_sort_max_rows(int M, int E, int k, int block);
+
+/* Capacity of expert_of_block: max_rows / block (rounded down), or -1. */
+int64_t moe_route_sort_max_blocks(int M, int E, int k, int block);
+
+/* Workspace bytes needed by any path for these sizes (0 when none is needed);
+ * (size_t)-1 for invalid sizes. */
+size_t moe_route_sort_workspace_bytes(int M, int E, int k, int block);
+
+/* Static text for an MRS_* code; never NULL. */
+const char* moe_route_sort_strerror(int code);
+
+/*
+ * Diagnostics: evaluate the two sigmoid forms the kernels use, elementwise on
+ * device arrays of n FP32 values: fast_out = the approximate form used to rank
+ * candidates, exact_out = the correctly rounded form used for weights and for
+ * exact decisions.  Asynchronous on stream.  Returns MRS_OK or an error code.
+ */
+int moe_route_sort_sigmoid_probe(const float* x, int n, float* fast_out, float* exact_out,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_SORT_H */

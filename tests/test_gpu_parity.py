@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Expert ids and all sort metadata must be bit-exact;
+weights within 1e-6 relative of the oracle's float64 weights.  Tokens whose
+k-th/(k+1)-th (or group-boundary) gap is below 1e-6 are counted and printed
+separately -- they are still required to match exactly."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import route_sort as orc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+amr = pytest.importorskip("align_moe_route_amd")
+
+W_RTOL = 1e-6
+
+
+def to_gpu(inp):
+    if inp.cfg.dtype == "bf16":
+        x = torch.from_numpy(inp.logits_storage.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x = torch.from_numpy(inp.logits_storage).cuda()
+    return x, torch.from_numpy(inp.bias).cuda()
+
+
+def fetch(out, block):
+    torch.cuda.synchronize()
+    npp = int(out.num_post_pad.item())
+    return dict(ids=out.ids.cpu().numpy(), w=out.weights.cpu().numpy(), npp=npp,
+                rows=out.sorted_ids[:npp].cpu().numpy(),
+                eob=out.expert_of_block[:npp // block].cpu().numpy())
+
+
+def run(inp, flags=0, stats=None):
+    cfg = inp.cfg
+    x, b = to_gpu(inp)
+    print(f"[gpu] {cfg.name} M={cfg.M} E={cfg.E} k={cfg.k} g={cfg.n_group}/{cfg.topk_group} "
+          f"block={cfg.block} {cfg.dtype} {cfg.dist} flags={flags}", flush=True)
+    out = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, flags=flags, stats=stats)
+    return fetch(out, cfg.block)
+
+
+def assert_metadata_matches_ids(g, cfg):
+    """The oracle's sort stage run on the GPU's own ids equals the GPU metadata
+    bit for bit, with no exemption."""
+    meta = orc.sort_metadata(g["ids"], cfg.E, cfg.block)
+    assert g["npp"] == meta.num_post_pad
+    assert np.array_equal(g["rows"], meta.sorted_ids)
+    assert np.array_equal(g["eob"], meta.expert_of_block)
+
+
+def assert_parity(inp, g, tokens=None):
+    cfg = inp.cfg
+    ref = orc.route_sort(inp.logits_storage, cfg.dtype, inp.bias, cfg.k, cfg.n_group,
+                         cfg.topk_group, cfg.block, tokens=tokens)
+    gi = g["ids"] if tokens is None else g["ids"][tokens]
+    gw = g["w"] if tokens is None else g["w"][tokens]
+    near = (ref.gap_k < 1e-6) | (ref.gap_g < 1e-6)
+    if near.any():
+        print(f"  near-tie tokens (gap < 1e-6): {int(near.sum())} of {near.size}", flush=True)
+    bad = np.flatnonzero(np.any(gi != ref.ids, axis=1))
+    assert bad.size == 0, f"{bad.size} tokens differ, first {bad[:5]} near-tie={near[bad[:5]]}"
+    err = np.abs(gw.astype(np.float64) - ref.weights) / np.abs(ref.weights)
+    assert err.max() <= W_RTOL, err.max()
+    if tokens is None:
+        assert g["npp"] == ref.meta.num_post_pad
+        assert np.array_equal(g["rows"], ref.meta.sorted_ids)
+        assert np.array_equal(g["eob"], ref.meta.expert_of_block)
+    assert_metadata_matches_ids(g, cfg)
+    assert orc.check_sort_invariants(g["ids"], g["rows"], g["eob"], g["npp"], cfg.E, cfg.block) == []
+    return ref
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_workload_parity(name):
+    cfg = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(cfg)
+    stats = torch.zeros(2, dtype=torch.int32, device="cuda")
+    g = run(inp, stats=stats)
+    st = stats.cpu().numpy()
+    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}", flush=True)
+    assert st.sum() == cfg.M
+    tokens = None if cfg.M * cfg.E <= 8192 * 896 else np.arange(0, cfg.M, 16)
+    assert_parity(inp, g, tokens)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "threshold", "prefill_skew"])
+def test_exact_path_parity(name):
+    """Every token through the workgroup-wide exact selection."""
+    cfg = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(cfg)
+    g = run(inp, flags=amr.FLAG_FORCE_EXACT)
+    tokens = None if cfg.M <= 512 else np.arange(0, cfg.M, 8)
+    assert_parity(inp, g, tokens)
+
+
+@pytest.mark.parametrize("name,flags", [("tiny", 2), ("decode", 2), ("tiny", 1), ("decode", 1),
+                                        ("decode", 6), ("tiny", 5)])
+def test_forced_paths(name, flags):
+    cfg = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(cfg)
+    assert_parity(inp, run(inp, flags=flags))
+
+
+# ---------------------------------------------------------------------------
+# Sweeps over shapes, group layouts, block sizes and distributions.
+# ---------------------------------------------------------------------------
+SWEEP = [
+    # M, E, k, n_group, topk_group, block, dtype, dist
+    (1, 64, 4, 8, 4, 16, "f32", "normal"),
+    (3, 64, 8, 64, 10, 1, "bf16", "normal"),         # group of one expert
+    (65, 128, 8, 2, 1, 32, "f32", "hot"),             # just past the single-workgroup bound
+    (63, 256, 16, 4, 2, 48, "bf16", "shared"),
+    (130, 512, 16, 8, 3, 64, "bf16", "dominant_group"),
+    (257, 896, 16, 8, 4, 128, "bf16", "log_zipf"),
+    (300, 896, 16, 1, 1, 16, "f32", "coarse"),        # many exact ties
+    (200, 896, 16, 8, 4, 32, "f32", "duplicated"),    # pairs of identical keys
+    (64, 896, 16, 8, 4, 32, "f32", "equal"),          # all keys equal
+    (100, 1024, 32, 16, 8, 64, "f32", "normal"),
+    (50, 2048, 64, 32, 16, 16, "bf16", "normal"),
+    (70, 4096, 16, 16, 8, 128, "f32", "normal"),
+    (33, 4096, 8, 64, 2, 8, "bf16", "normal"),
+    # shapes outside the wave layout: every token takes the exact selection
+    (40, 100, 5, 5, 2, 7, "f32", "normal"),
+    (20, 129, 5, 1, 1, 16, "bf16", "shared"),
+    (17, 3000, 12, 12, 5, 20, "f32", "normal"),
+    (9, 4095, 3, 3, 1, 3, "bf16", "hot"),
+    (90, 768, 6, 96, 10, 24, "f32", "normal"),       # 96 groups of 8
+    (12, 17, 1, 1, 1, 1, "f32", "normal"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "M{}_E{}_k{}_g{}-{}_b{}_{}_{}".format(*c))
+def test_sweep_parity(case):
+    M, E, k, ng, tg, block, dtype, dist = case
+    cfg = workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=M + E)
+    inp = workloads.make_inputs(cfg)
+    assert_parity(inp, run(inp))
+
+
+@pytest.mark.parametrize("dist", ["normal", "hot", "shared", "dominant_group", "log_zipf", "equal",
+                                  "duplicated", "coarse"])
+def test_distributions_prefill_shape(dist):
+    cfg = workloads.custom(1024, 896, 16, 8, 4, 128, "bf16", dist, seed=7)
+    inp = workloads.make_inputs(cfg)
+    assert_parity(inp, run(inp))
+
+
+# ---------------------------------------------------------------------------
+# Contract: untouched tails, zero tokens, immutability, reuse, determinism,
+# graph replay with changed inputs.
+# ---------------------------------------------------------------------------
+def test_poisoned_outputs_tails_untouched():
+    cfg = workloads.custom(300, 896, 16, 8, 4, 64, "bf16", "log_zipf", seed=3)
+    inp = workloads.make_inputs(cfg)
+    x, b = to_gpu(inp)
+    rows, blocks = amr.max_rows(cfg.M, cfg.E, cfg.k, cfg.block), amr.max_blocks(cfg.M, cfg.E, cfg.k, cfg.block)
+    poison = -123456
+    out = amr.RouteSortOutput(
+        torch.full((cfg.M, cfg.k), poison, dtype=torch.int32, device="cuda"),
+        torch.full((cfg.M, cfg.k), float("nan"), dtype=torch.float32, device="cuda"),
+        torch.full((rows + 64,), poison, dtype=torch.int32, device="cuda"),
+        torch.full((blocks + 64,), poison, dtype=torch.int32, device="cuda"),
+        torch.full((1,), poison, dtype=torch.int32, device="cuda"))
+    x0, b0 = x.clone(), b.clone()
+    amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    g = fetch(out, cfg.block)
+    assert_parity(inp, g)
+    rows_all = out.sorted_ids.cpu().numpy()
+    eob_all = out.expert_of_block.cpu().numpy()
+    assert np.all(rows_all[g["npp"]:] == poison)
+    assert np.all(eob_all[g["npp"] // cfg.block:] == poison)
+    assert torch.equal(x, x0) and torch.equal(b, b0)   # inputs never written
+
+
+def test_zero_tokens():
+    x = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    b = torch.zeros(64, dtype=torch.float32, device="cuda")
+    out = amr.RouteSortOutput(torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                              torch.empty((0, 4), dtype=torch.float32, device="cuda"),
+                              torch.full((4,), 7, dtype=torch.int32, device="cuda"),
+                              torch.full((4,), 7, dtype=torch.int32, device="cuda"),
+                              torch.full((1,), 7, dtype=torch.int32, device="cuda"))
+    amr.route_sort(x, b, 4, 8, 4, 16, out=out)
+    torch.cuda.synchronize()
+    assert int(out.num_post_pad.item()) == 0
+    assert torch.all(out.sorted_ids == 7) and torch.all(out.expert_of_block == 7)
+
+
+def test_determinism_across_runs_and_paths():
+    cfg = workloads.custom(700, 896, 16, 8, 4, 128, "bf16", "log_zipf", seed=21)
+    inp = workloads.make_inputs(cfg)
+    base = run(inp)
+    for flags in [0] * 10 + [amr.FLAG_FORCE_EXACT, amr.FLAG_FORCE_MULTI_WG]:
+        g = run(inp, flags=flags)
+        for key in ("ids", "rows", "eob"):
+            assert np.array_equal(g[key], base[key])
+        assert np.array_equal(g["w"].view(np.uint32), base["w"].view(np.uint32)) or flags
+
+
+def test_graph_replay_with_changed_inputs():
+    cfg = workloads.custom(512, 896, 16, 8, 4, 64, "bf16", "normal", seed=30)
+    sets = [workloads.make_inputs(cfg, seed=s) for s in range(4)]
+    x, b = to_gpu(sets[0])
+    out = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)  # warm up, allocate
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    for rep in range(8):
+        inp = sets[rep % 4]
+        xs, bs = to_gpu(inp)
+        x.copy_(xs)
+        b.copy_(bs)
+        torch.cuda.synchronize()
+        graph.replay()
+        g = fetch(out, cfg.block)
+        assert_parity(inp, g)
+
+
+def test_stats_count_every_token():
+    cfg = workloads.CONFIGS["threshold"]
+    inp = workloads.make_inputs(cfg)
+    stats = torch.zeros(2, dtype=torch.int32, device="cuda")
+    run(inp, stats=stats)
+    run(inp, flags=amr.FLAG_FORCE_EXACT, stats=stats)
+    st = stats.cpu().numpy()
+    assert st.sum() == 2 * cfg.M and st[0] >= cfg.M
+
+
+# ---------------------------------------------------------------------------
+# The two sigmoid forms of the kernels.
+# ---------------------------------------------------------------------------
+def test_exact_sigmoid_bit_exact_on_all_bf16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = orc.bf16_bits_to_f32(bits)
+    x = x[np.isfinite(x)]
+    f, e = amr.sigmoid_probe(torch.from_numpy(x).cuda())
+    ref = orc.sigmoid_f32(x)
+    e = e.cpu().numpy()
+    bad = np.flatnonzero(e.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, (x[bad[:8]], e[bad[:8]], ref[bad[:8]])
+    err = np.abs(f.cpu().numpy().astype(np.float64) - ref.astype(np.float64))
+    print(f"  fast sigmoid max |err| over BF16 inputs: {err.max():.3e}", flush=True)
+    assert err.max() < 2.0 ** -22
+
+
+def test_sigmoid_forms_on_fp32_grid():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([np.linspace(-110, 40, 400001), rng.standard_normal(200000) * 3,
+                        rng.standard_normal(50000) * 1e-3, rng.standard_normal(50000) * 1e-6]
+                       ).astype(np.float32)
+    f, e = amr.sigmoid_probe(torch.from_numpy(x).cuda())
+    ref = orc.sigmoid_f32(x)
+    e = e.cpu().numpy()
+    mism = np.flatnonzero(e.view(np.uint32) != ref.view(np.uint32))
+    print(f"  exact-form mismatches on {x.size} FP32 inputs: {mism.size}", flush=True)
+    assert mism.size <= 2  # residual float64 rounding-window cases, 1 ulp each
+    if mism.size:
+        assert np.all(np.abs(e[mism].view(np.int32) - ref[mism].view(np.int32)) == 1)
+    err = np.abs(f.cpu().numpy().astype(np.float64) - ref.astype(np.float64))
+    print(f"  fast sigmoid max |err| over FP32 grid: {err.max():.3e}", flush=True)
+    assert err.max() < 2.0 ** -22

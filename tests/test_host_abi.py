@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes its buffers by the documented formulas, and rejects
+invalid calls with the documented codes before any launch.  No call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import align_moe_route_amd as amr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route_sort.h")
+
+# aligned fake device addresses: never dereferenced, validation fails first
+P = 0x10000
+Q = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_route_sort\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = amr.lib()
+    names = declared_functions()
+    assert set(names) == set(amr.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_names_every_code():
+    for c in range(-6, 1):
+        s = amr.strerror(c)
+        assert s and "unknown" not in s
+    assert "unknown" in amr.strerror(-99)
+
+
+def test_capacity_formulas():
+    for M, E, k, block in [(1, 896, 16, 32), (8192, 896, 16, 128), (16384, 4096, 16, 128),
+                           (4, 64, 4, 16), (0, 8, 2, 4), (3, 2, 2, 1), (512, 896, 16, 64)]:
+        routes = M * k
+        rows = routes + min(E, routes) * (block - 1)
+        assert amr.max_rows(M, E, k, block) == rows
+        assert amr.max_blocks(M, E, k, block) == rows // block
+    assert amr.max_rows(1, 896, 16, 32) == 512                      # decode: exactly 512 rows
+    assert amr.max_rows(2 ** 26, 4096, 64, 1) == -1                 # M*k overflows int32
+    assert amr.max_rows(1 << 20, 4096, 16, 1 << 20) == -1           # padding overflows
+    assert amr.max_rows(1, 0, 1, 1) == -1 and amr.max_rows(1, 8, 1, 0) == -1
+
+
+def test_workspace_sizes():
+    assert amr.workspace_bytes(0, 896, 16, 128) == 0
+    a = amr.workspace_bytes(8192, 896, 16, 128)
+    b = amr.workspace_bytes(16384, 4096, 16, 128)
+    assert a > 0 and b > a
+    # linear in the number of workgroup histogram rows: bounded by a few MB
+    assert b < 16 << 20
+    with pytest.raises(ValueError):
+        amr.workspace_bytes(1, 5000, 1, 1)
+
+
+def call(M=4, E=64, k=4, n_group=8, topk_group=4, block=16, logits=P, bias=P, ids=P, w=P,
+         rows=P, eob=P, npp=P, dtype=0, ws=Q, ws_bytes=1 << 30, flags=0, stats=None):
+    return amr.raw_call(logits, bias, M, E, k, n_group, topk_group, block, ids, w, rows, eob,
+                        npp, dtype, ws, ws_bytes, None, flags, stats)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(E=0), dict(E=4097, n_group=1, topk_group=1), dict(n_group=7),
+    dict(n_group=0), dict(topk_group=0), dict(topk_group=9), dict(k=0), dict(k=65, E=128),
+    dict(k=33, n_group=8, topk_group=4),     # only 4 groups x 8 experts = 32 candidates
+    dict(block=0), dict(dtype=2), dict(dtype=-1), dict(flags=8), dict(flags=3),
+    dict(M=100, flags=1),                     # single workgroup cannot take 100 tokens
+])
+def test_invalid_arguments(kw):
+    assert call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_overflow():
+    assert call(M=2 ** 26, E=4096, k=64, n_group=1, topk_group=1, block=1) == amr.MRS_ERR_OVERFLOW
+    assert call(M=1 << 20, E=4096, k=16, n_group=1, topk_group=1, block=1 << 20) == amr.MRS_ERR_OVERFLOW
+
+
+@pytest.mark.parametrize("name", ["logits", "bias", "ids", "w", "rows", "eob", "npp"])
+def test_null_pointers(name):
+    assert call(**{name: None}) == amr.MRS_ERR_NULL_POINTER
+
+
+def test_zero_tokens_needs_only_num_post_pad():
+    assert call(M=0, npp=None) == amr.MRS_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("name,off", [("logits", 8), ("logits", 4), ("bias", 2), ("ids", 2),
+                                      ("w", 1), ("rows", 2), ("eob", 3), ("npp", 2)])
+def test_misaligned(name, off):
+    assert call(**{name: P + off}) == amr.MRS_ERR_MISALIGNED
+
+
+def test_workspace_checks():
+    big = dict(M=8192, E=896, k=16, n_group=8, topk_group=4, block=128)
+    need = amr.workspace_bytes(8192, 896, 16, 128)
+    assert call(**big, ws=None) == amr.MRS_ERR_WORKSPACE
+    assert call(**big, ws_bytes=need - 4) == amr.MRS_ERR_WORKSPACE
+    assert call(**big, ws=Q + 4) == amr.MRS_ERR_MISALIGNED
+    # a small call forced onto the multi-workgroup path needs the workspace too
+    assert call(M=4, flags=amr.FLAG_FORCE_MULTI_WG, ws=None) == amr.MRS_ERR_WORKSPACE
+
+
+def test_sigmoid_probe_validation():
+    L = amr.lib()
+    assert L.moe_route_sort_sigmoid_probe(P, -1, P, P, None) == amr.MRS_ERR_INVALID_ARG
+    assert L.moe_route_sort_sigmoid_probe(P, 0, P, P, None) == amr.MRS_OK
+    assert L.moe_route_sort_sigmoid_probe(None, 5, P, P, None) == amr.MRS_ERR_NULL_POINTER
+    assert L.moe_route_sort_sigmoid_probe(P + 2, 5, P, P, None) == amr.MRS_ERR_MISALIGNED
