@@ -6,27 +6,34 @@
 // block-padded dispatch metadata for a grouped GEMM.  Exact definitions of
 // every output are in include/moe_route_sort.h.
 //
-// Structure
-//   selection   one wave64 per token.  Keys are ranked with a fast sigmoid
-//               (v_exp_f32 + v_rcp_f32) whose error is bounded; a token whose
-//               k-th/(k+1)-th key gap or group-boundary gap is wider than that
-//               bound is decided exactly by the fast ranking ("certified").
-//               Every other token -- and every token of a shape the wave
-//               layout does not cover -- is re-decided by the whole workgroup
-//               from correctly rounded keys.  Weights always use the correctly
-//               rounded sigmoid.
-//   histogram   per-workgroup LDS bitsets: bit tl of word e is set when the
-//               workgroup's token tl picked expert e.  The popcount is the
-//               workgroup's histogram (replacing one contended global atomic
-//               per route, as on the page "gfx1250 ordinary-TP route
-//               optimization", Summary), and the popcount of the bits below tl
-//               is the slot's stable rank inside the workgroup.
-//   prefix      column scan of the workgroup histograms in workgroup order,
-//               then an exclusive scan of the padded per-expert totals.
-//   scatter     slot -> off[e] + (routes to e in earlier workgroups) +
-//               (earlier tokens of this workgroup with e): a stable counting
-//               sort, so the order never depends on scheduling.
-// Small calls (M <= 64) run everything in one workgroup and one launch.
+// Selection (one wave64 per token; lane l owns experts [l*epl, (l+1)*epl))
+//   1. keys A = fast_sigmoid(x) + b for all experts (|A - exact key| <= delta)
+//      and each lane's top two keys;
+//   2. group stage: top-2 merged across the lanes of a group with DPP, group
+//      score, rank of every group by (score desc, index asc); the boundary is
+//      accepted only if the topk_group-th and next scores differ by more than
+//      the error of the fast scores, else the token is redone with exact keys;
+//   3. threshold tau0 = k-th largest lane maximum among the kept lanes (at
+//      least k keys reach it), by a short bisection from the highest differing
+//      bit; every exact top-k expert has A >= tau0 - 2*delta;
+//   4. the (typically ~20, at most 64) candidates above that line are
+//      compacted in expert order; each candidate lane computes its correctly
+//      rounded sigmoid and exact key; exact ranks by (key desc, index asc)
+//      pick the k experts, so the result is exact without any tie exemption;
+//   5. weights from the same exact sigmoid values, normalised in float64.
+//   A token with more than 64 candidates (heavy exact ties) and every token of
+//   a shape outside this layout is decided by the whole workgroup from exact
+//   keys held in LDS.
+// Histogram and ranks: per-workgroup LDS bitsets, bit tl of word e set when
+//   token tl of the workgroup picked expert e.  Popcount = the workgroup's
+//   count for e (no global atomic per route; compare the workgroup histograms
+//   of the page "gfx1250 ordinary-TP route optimization", Summary); popcount
+//   of the bits below tl = the slot's stable rank inside the workgroup.
+// Large M: three launches -- select (+ histogram row, slot records), column
+//   scan of the histograms in workgroup order, scatter.  On MI355X a device-
+//   wide barrier inside one launch costs tens of microseconds (agent-scope
+//   release/acquire across the eight XCDs), far more than a kernel boundary.
+// M <= 64: everything in one workgroup and one launch.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -37,22 +44,26 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWG = 256;                 // threads per workgroup, all kernels
-constexpr int kNWaves = kWG / kWave;
+constexpr int kNW = 8;                   // waves per workgroup
+constexpr int kWG = kNW * kWave;         // threads per workgroup, all kernels
 constexpr int kTwMax = 64;               // tokens per workgroup: one bit each in a 64-bit word
 constexpr int kEMax = 4096;              // 16 KiB of 32-bit counters, the pages' LDS bound
-constexpr int kEptMax = kEMax / kWG;     // experts per thread in the exact selection
-constexpr int kSmallSlotsMax = 2048;     // M*k bound of the single-workgroup path
-constexpr size_t kLdsLimit = 64 * 1024;
+constexpr int kBiasRegMax = 16;          // lanes keep their biases in registers up to this many experts
+constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kWsHeader = 256;
+constexpr int kCandMax = kWave;          // candidates per token in the wave path
 
 enum { KIND_SMALL = 0, KIND_SELECT = 1, KIND_SCATTER = 2 };
+enum { LOAD_VEC = 0, LOAD_STAGE = 1 };
+enum { TOK_DONE = 0, TOK_REDO_EXACT = 1, TOK_ESCALATE = 2 };
 
 struct Args {
   const void* logits;
   const float* bias;
   int M, E, k, n_group, topk_group, block;
   int G;       // experts per group
+  int epl;     // experts per lane in the wave path (E / 64)
+  int lpg;     // lanes per group in the wave path (64 / n_group)
   int tw;      // tokens per workgroup
   int nwg;     // workgroups of the multi-workgroup path
   int fast;    // the wave layout covers this shape
@@ -62,9 +73,10 @@ struct Args {
   int32_t* sorted_ids;
   int32_t* eob;
   int32_t* npp;
-  int32_t* ws_cnt;   // [E]
-  int32_t* ws_pad;   // [E]
-  int32_t* ws_hist;  // [nwg][E]
+  int32_t* ws_tot;   // [E] routes per expert
+  int32_t* ws_pad;   // [E] padded routes per expert
+  int32_t* ws_hist;  // [nwg][E] per-workgroup counts, then exclusive column prefixes
+  int32_t* ws_slot;  // [M*k] expert | (rank inside the workgroup << 16)
   int32_t* stats;
 };
 
@@ -72,26 +84,35 @@ struct Args {
 // LDS plan shared by host (size) and device (carving).
 // ----------------------------------------------------------------------------
 struct LdsPlan {
-  size_t bits, redd, off, ids, cand_a, cand_i, esc, grp, misc, red, scan, total;
+  size_t bits, redd, off, ids, cand_i, cand_c, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
-__host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gstage, int tw, int k) {
+__host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gstage, int fast,
+                                            int stage_bytes, int tw, int k) {
   LdsPlan p{};
   size_t o = 0;
-  p.bits = o; o += (size_t)E * 8;
-  p.redd = o; o += (size_t)kNWaves * 8;
-  if (kind != KIND_SELECT) { p.off = o; o += (size_t)E * 4; }
-  if (kind == KIND_SMALL) { p.ids = o; o += (size_t)tw * k * 4; }
+  auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
+  if (kind != KIND_SCATTER) p.bits = take((size_t)E * 8);
+  p.redd = take((size_t)kNW * 8);
+  if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
   if (kind != KIND_SCATTER) {
-    p.cand_a = o; o += (size_t)kNWaves * kWave * 4;
-    p.cand_i = o; o += (size_t)kNWaves * kWave * 4;
-    p.esc = o; o += (size_t)kTwMax * 4;
-    p.grp = o; o += gstage ? (size_t)3 * n_group * 4 : 0;
+    p.ids = take((size_t)tw * k * 4);
+    p.cand_c = take((size_t)kNW * kCandMax * 8);
+    p.cand_i = take((size_t)kNW * kCandMax * 4);
+    // union: wave staging buffers (fast loop) / exact keys + group arrays (after it)
+    const size_t stage = fast ? (size_t)kNW * stage_bytes : 0;
+    const size_t ex = (size_t)E * 4 + (gstage ? (size_t)3 * n_group * 4 + 16 : 0);
+    const size_t un = stage > ex ? stage : ex;
+    p.u = take(un);
+    p.stage = p.u;
+    p.ukey = p.u;
+    p.grp = p.u + (((size_t)E * 4 + 15) & ~(size_t)15);
+    p.esc = take((size_t)kTwMax * 4);
   }
-  p.misc = o; o += 16 * 4;
-  p.red = o; o += (size_t)2 * kNWaves * 4;
-  p.scan = o; o += (size_t)kNWaves * 4;
-  p.total = (o + 15) & ~(size_t)15;
+  p.misc = take(16 * 4);
+  p.red = take((size_t)2 * kNW * 4);
+  p.scan = take((size_t)kNW * 4);
+  p.total = o;
   return p;
 }
 
@@ -100,31 +121,37 @@ struct Lds {
   double* redd;
   int* off;
   int* ids;
-  float* cand_a;
+  unsigned long long* cand_c;
   int* cand_i;
-  int* esc;
+  unsigned char* stage;
+  uint32_t* ukey;
   unsigned* grp;
+  int* esc;
   int* misc;
   int* red;
   int* scan;
+  int stage_bytes;
 };
 
 extern __shared__ __align__(16) unsigned char g_lds[];
 
-__device__ inline Lds carve(int kind, const Args& a) {
-  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, a.tw, a.k);
+__device__ inline Lds carve(int kind, const Args& a, int stage_bytes) {
+  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, a.fast, stage_bytes, a.tw, a.k);
   Lds L;
   L.bits = reinterpret_cast<unsigned long long*>(g_lds + p.bits);
   L.redd = reinterpret_cast<double*>(g_lds + p.redd);
   L.off = reinterpret_cast<int*>(g_lds + p.off);
   L.ids = reinterpret_cast<int*>(g_lds + p.ids);
-  L.cand_a = reinterpret_cast<float*>(g_lds + p.cand_a);
+  L.cand_c = reinterpret_cast<unsigned long long*>(g_lds + p.cand_c);
   L.cand_i = reinterpret_cast<int*>(g_lds + p.cand_i);
-  L.esc = reinterpret_cast<int*>(g_lds + p.esc);
+  L.stage = g_lds + p.stage;
+  L.ukey = reinterpret_cast<uint32_t*>(g_lds + p.ukey);
   L.grp = reinterpret_cast<unsigned*>(g_lds + p.grp);
+  L.esc = reinterpret_cast<int*>(g_lds + p.esc);
   L.misc = reinterpret_cast<int*>(g_lds + p.misc);
   L.red = reinterpret_cast<int*>(g_lds + p.red);
   L.scan = reinterpret_cast<int*>(g_lds + p.scan);
+  L.stage_bytes = stage_bytes;
   return L;
 }
 
@@ -162,9 +189,9 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 
 // Fast sigmoid for ranking: 1 / (1 + 2^(-x*log2(e))) with the hardware
 // exp2 and reciprocal.  Its distance to the correctly rounded sigmoid is below
-// 2^-21 for every FP32 x (about 2.6e-7 from the error terms: argument rounding,
-// 1-ulp exp2, rounding of 1+e, 1-ulp reciprocal); the certification margins
-// below are built on 2^-21.
+// 2^-21 for every FP32 x (error terms: argument rounding, 1-ulp exp2,
+// rounding of 1+e, 1-ulp reciprocal: about 2.6e-7; measured on MI355X below
+// 1.2e-7); the margins of the selection are built on 2^-21.
 __device__ __forceinline__ float sigmoid_fast(float x) {
   const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896341f);
   return __builtin_amdgcn_rcpf(1.0f + e);
@@ -176,7 +203,7 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 // there the series 1/2 + x/4 - x^3/48 + x^5/480 is split into an exact head
 // and a small tail and the rounding side is read off their sum.  Elsewhere
 // RN32 of the float64 value 1 / (1 + exp(-x)).
-__device__ __noinline__ float sigmoid_exact(float x) {
+__device__ __forceinline__ float sigmoid_exact(float x) {
   const double xd = (double)x;
   if (fabs(xd) < 0x1p-10) {
     const double hi = 0.5 + 0.25 * xd;  // exact for |x| >= 2^-29; else far from a midpoint
@@ -201,45 +228,81 @@ __device__ __noinline__ float sigmoid_exact(float x) {
 }
 
 // ----------------------------------------------------------------------------
-// Wave-level helpers (wave64).
+// Wave-level helpers (wave64, DPP row shifts and broadcasts).
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// m-th largest of the per-lane values v (lanes that do not take part pass 0;
-// at least m lanes take part).  Bitwise bisection: one compare + ballot per bit.
-__device__ __forceinline__ uint32_t wave_kth(uint32_t v, int m) {
-  uint32_t T = 0;
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    if (__popcll(__ballot(v >= c)) >= m) T = c;
-  }
-  return T;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
+// Inclusive prefix sum over the wave (row shifts 1,2,4,8 then row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  uint32_t u = (uint32_t)v;
+  u += dpp<kRowShr1>(0u, u);
+  u += dpp<kRowShr2>(0u, u);
+  u += dpp<kRowShr4>(0u, u);
+  u += dpp<kRowShr8>(0u, u);
+  u += dpp<kRowBcast15, 0xA>(0u, u);
+  u += dpp<kRowBcast31, 0xC>(0u, u);
+  return (int)u;
+}
+__device__ __forceinline__ int wave_sum_i(int v) { return (int)readlane((uint32_t)wave_incl_scan(v), 63); }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
+  u = max(u, dpp<kRowShr1>(0u, u));
+  u = max(u, dpp<kRowShr2>(0u, u));
+  u = max(u, dpp<kRowShr4>(0u, u));
+  u = max(u, dpp<kRowShr8>(0u, u));
+  u = max(u, dpp<kRowBcast15, 0xA>(0u, u));
+  u = max(u, dpp<kRowBcast31, 0xC>(0u, u));
+  return readlane(u, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t u) {
+  u = min(u, dpp<kRowShr1>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr2>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr4>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr8>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowBcast15, 0xA>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowBcast31, 0xC>(0xFFFFFFFFu, u));
+  return readlane(u, 63);
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
+  auto step = [](double x, auto sh) {
+    const uint64_t b = __double_as_longlong(x);
+    const uint32_t lo = sh((uint32_t)b), hi = sh((uint32_t)(b >> 32));
+    return x + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  v = step(v, [](uint32_t u) { return dpp<kRowShr1>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr2>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr4>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr8>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowBcast15, 0xA>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowBcast31, 0xC>(0u, u); });
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = readlane((uint32_t)b, 63), hi = readlane((uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(v, d);
-    if (l >= d) v += y;
+
+// Partner for level `lev` of a butterfly over aligned blocks of 2^(lev+1)
+// lanes: lanes of the two halves of each block meet pairwise.
+__device__ __forceinline__ float butterfly_partner(float v, int lev) {
+  const uint32_t u = __float_as_uint(v);
+  switch (lev) {
+    case 0: return __uint_as_float(dpp<kQuadXor1>(u, u));
+    case 1: return __uint_as_float(dpp<kQuadXor2>(u, u));
+    case 2: return __uint_as_float(dpp<kRowHalfMirror>(u, u));
+    case 3: return __uint_as_float(dpp<kRowMirror>(u, u));
+    default: return __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F));  // xor 16
   }
-  return v;
 }
 
 // ----------------------------------------------------------------------------
@@ -262,61 +325,59 @@ __device__ double wg_sum_d(const Lds& L, double v) {
   if (lane_id() == 0) L.redd[w] = v;
   __syncthreads();
   double s = 0.0;
-  for (int q = 0; q < kNWaves; ++q) s += L.redd[q];
+  for (int q = 0; q < kNW; ++q) s += L.redd[q];
   __syncthreads();
   return s;
 }
 
-__device__ float wg_max_f(const Lds& L, float v) {
+__device__ uint32_t wg_max_u32(const Lds& L, uint32_t v) {
   const int w = threadIdx.x >> 6;
-  v = wave_max_f(v);
-  if (lane_id() == 0) L.red[w] = __float_as_int(v);
+  v = wave_max_u32(v);
+  if (lane_id() == 0) L.red[w] = (int)v;
   __syncthreads();
-  float m = v;
-  for (int q = 0; q < kNWaves; ++q) m = fmaxf(m, __int_as_float(L.red[q]));
+  uint32_t m = 0;
+  for (int q = 0; q < kNW; ++q) m = max(m, (uint32_t)L.red[q]);
   __syncthreads();
   return m;
 }
 
-// Number of (mask-selected) values >= c over the workgroup.  `parity` picks
-// one of two LDS buffers so consecutive calls need a single barrier each.
-__device__ __forceinline__ int wg_count_ge(const Lds& L, const uint32_t* u, uint32_t mask, uint32_t c,
-                                           int parity) {
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i) n += __popcll(__ballot(((mask >> i) & 1u) && u[i] >= c));
+// Number of selected entries >= c among arr[i0 + i] (i < n, bit i of mask).
+__device__ __forceinline__ int wg_count_ge(const Lds& L, const uint32_t* arr, int i0, int n, uint32_t mask,
+                                           uint32_t c, int parity) {
+  int cnt = 0;
+  for (int i = 0; i < n; ++i) cnt += (((mask >> i) & 1u) && arr[i0 + i] >= c) ? 1 : 0;
+  const int s = wave_sum_i(cnt);
   const int w = threadIdx.x >> 6;
-  if (lane_id() == 0) L.red[parity * kNWaves + w] = n;
+  if (lane_id() == 0) L.red[parity * kNW + w] = s;
   __syncthreads();
-  int s = 0;
-  for (int q = 0; q < kNWaves; ++q) s += L.red[parity * kNWaves + q];
-  return s;
+  int t = 0;
+  for (int q = 0; q < kNW; ++q) t += L.red[parity * kNW + q];
+  return t;
 }
 
-// Select the m largest values (ties to the lower index) among the mask-
-// selected entries; thread r holds entries [r*n, (r+1)*n) in index order.
-// Returns this thread's selection bits.
-__device__ uint32_t wg_select(const Lds& L, const uint32_t* u, uint32_t mask, int m) {
+// Select the m largest of the mask-selected entries (ties to the lower index);
+// thread r holds entries [i0, i0+n) of arr in index order.  Returns this
+// thread's selection bits.
+__device__ uint32_t wg_select(const Lds& L, const uint32_t* arr, int i0, int n, uint32_t mask, int m) {
   uint32_t T = 0;
   int parity = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = T | (1u << b);
-    if (wg_count_ge(L, u, mask, c, parity) >= m) T = c;
+    if (wg_count_ge(L, arr, i0, n, mask, c, parity) >= m) T = c;
     parity ^= 1;
   }
-  const int gt = (T == 0xFFFFFFFFu) ? 0 : wg_count_ge(L, u, mask, T + 1u, parity);
+  const int gt = (T == 0xFFFFFFFFu) ? 0 : wg_count_ge(L, arr, i0, n, mask, T + 1u, parity);
   const int r = m - gt;  // equal values to take, lowest index first
   uint32_t sel = 0, tie = 0;
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i) {
+  for (int i = 0; i < n; ++i) {
     if ((mask >> i) & 1u) {
-      if (u[i] > T) sel |= 1u << i;
-      else if (u[i] == T) tie |= 1u << i;
+      const uint32_t v = arr[i0 + i];
+      if (v > T) sel |= 1u << i;
+      else if (v == T) tie |= 1u << i;
     }
   }
   int rank = wg_excl_scan(L, __popc(tie));
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i) {
+  for (int i = 0; i < n; ++i) {
     if ((tie >> i) & 1u) {
       if (rank < r) sel |= 1u << i;
       ++rank;
@@ -326,49 +387,42 @@ __device__ uint32_t wg_select(const Lds& L, const uint32_t* u, uint32_t mask, in
 }
 
 // ----------------------------------------------------------------------------
-// Exact selection of one token by the whole workgroup (correctly rounded keys).
-// Thread r owns experts [r*ept, (r+1)*ept).
+// Exact selection of one token by the whole workgroup (correctly rounded keys
+// in LDS).  Thread r owns experts [r*ept, (r+1)*ept).
 // ----------------------------------------------------------------------------
 template <bool BF16>
-__device__ void exact_token(const Args& a, const Lds& L, int t, int tl, int* ids_cache) {
+__device__ void exact_token_wg(const Args& a, const Lds& L, int t, int tl, int* ids_cache) {
   const int tid = threadIdx.x;
   const int E = a.E, G = a.G;
-  const int ept = (E + kWG - 1) / kWG;
-  const int e0 = tid * ept;
   const size_t row = (size_t)t * E;
-  uint32_t u[kEptMax];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i) {
-    u[i] = 0;
-    const int e = e0 + i;
-    if (i < ept && e < E) {
-      const float s = sigmoid_exact(load_logit<BF16>(a.logits, row + e));
-      u[i] = f2s(s + a.bias[e]);
-      valid |= 1u << i;
-    }
+  uint32_t* uk = L.ukey;
+  for (int e = tid; e < E; e += kWG) {
+    const float s = sigmoid_exact(load_logit<BF16>(a.logits, row + e));
+    uk[e] = f2s(s + a.bias[e]);
   }
+  const int ept = (E + kWG - 1) / kWG;
+  const int e0 = min(E, tid * ept);
+  const int n = min(ept, E - e0);
+  const uint32_t valid = n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
+  __syncthreads();
   uint32_t allow = valid;
   if (a.gstage) {
     unsigned* gmax = L.grp;
-    unsigned* gsc = L.grp + a.n_group;   // count of the maximum, then the group score
+    unsigned* gsc = L.grp + a.n_group;       // count of the maximum, then the group score
     unsigned* gsec = L.grp + 2 * a.n_group;  // largest value below the maximum, then the flags
     for (int g = tid; g < a.n_group; g += kWG) { gmax[g] = 0u; gsc[g] = 0u; gsec[g] = 0u; }
     __syncthreads();
     {  // group maxima
       int cg = -1;
       uint32_t cm = 0;
-#pragma unroll
-      for (int i = 0; i < kEptMax; ++i) {
-        if ((valid >> i) & 1u) {
-          const int g = (e0 + i) / G;
-          if (g != cg) {
-            if (cg >= 0) atomicMax(&gmax[cg], cm);
-            cg = g;
-            cm = 0;
-          }
-          cm = u[i] > cm ? u[i] : cm;
+      for (int i = 0; i < n; ++i) {
+        const int g = (e0 + i) / G;
+        if (g != cg) {
+          if (cg >= 0) atomicMax(&gmax[cg], cm);
+          cg = g;
+          cm = 0;
         }
+        cm = max(cm, uk[e0 + i]);
       }
       if (cg >= 0) atomicMax(&gmax[cg], cm);
     }
@@ -376,23 +430,21 @@ __device__ void exact_token(const Args& a, const Lds& L, int t, int tl, int* ids
     {  // how often the maximum occurs, and the largest value below it
       int cg = -1;
       uint32_t gm = 0, c = 0, m2 = 0;
-#pragma unroll
-      for (int i = 0; i < kEptMax; ++i) {
-        if ((valid >> i) & 1u) {
-          const int g = (e0 + i) / G;
-          if (g != cg) {
-            if (cg >= 0) {
-              if (c) atomicAdd(&gsc[cg], c);
-              if (m2) atomicMax(&gsec[cg], m2);
-            }
-            cg = g;
-            gm = gmax[g];
-            c = 0;
-            m2 = 0;
+      for (int i = 0; i < n; ++i) {
+        const int g = (e0 + i) / G;
+        if (g != cg) {
+          if (cg >= 0) {
+            if (c) atomicAdd(&gsc[cg], c);
+            if (m2) atomicMax(&gsec[cg], m2);
           }
-          if (u[i] == gm) ++c;
-          else m2 = u[i] > m2 ? u[i] : m2;
+          cg = g;
+          gm = gmax[g];
+          c = 0;
+          m2 = 0;
         }
+        const uint32_t v = uk[e0 + i];
+        if (v == gm) ++c;
+        else m2 = max(m2, v);
       }
       if (cg >= 0) {
         if (c) atomicAdd(&gsc[cg], c);
@@ -407,178 +459,241 @@ __device__ void exact_token(const Args& a, const Lds& L, int t, int tl, int* ids
     }
     __syncthreads();
     const int gpt = (a.n_group + kWG - 1) / kWG;
-    const int g0 = tid * gpt;
-    uint32_t gu[kEptMax];
-    uint32_t gval = 0;
-#pragma unroll
-    for (int i = 0; i < kEptMax; ++i) {
-      gu[i] = 0;
-      if (i < gpt && g0 + i < a.n_group) {
-        gu[i] = gsc[g0 + i];
-        gval |= 1u << i;
-      }
-    }
-    const uint32_t gsel = wg_select(L, gu, gval, a.topk_group);
-#pragma unroll
-    for (int i = 0; i < kEptMax; ++i)
-      if ((gval >> i) & 1u) gsec[g0 + i] = (gsel >> i) & 1u;
+    const int g0 = min(a.n_group, tid * gpt);
+    const int gn = min(gpt, a.n_group - g0);
+    const uint32_t gval = gn >= 32 ? 0xFFFFFFFFu : ((1u << gn) - 1u);
+    const uint32_t gsel = wg_select(L, gsc, g0, gn, gval, a.topk_group);
+    for (int i = 0; i < gn; ++i) gsec[g0 + i] = (gsel >> i) & 1u;
     __syncthreads();
     allow = 0;
-#pragma unroll
-    for (int i = 0; i < kEptMax; ++i)
-      if (((valid >> i) & 1u) && gsec[(e0 + i) / G]) allow |= 1u << i;
+    for (int i = 0; i < n; ++i)
+      if (gsec[(e0 + i) / G]) allow |= 1u << i;
     __syncthreads();
   }
-  const uint32_t sel = wg_select(L, u, allow, a.k);
+  const uint32_t sel = wg_select(L, uk, e0, n, allow, a.k);
   double part = 0.0;
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i)
+  for (int i = 0; i < n; ++i)
     if ((sel >> i) & 1u) part += (double)sigmoid_exact(load_logit<BF16>(a.logits, row + e0 + i));
   const double ssum = wg_sum_d(L, part);
   int pos = wg_excl_scan(L, __popc(sel));
-#pragma unroll
-  for (int i = 0; i < kEptMax; ++i) {
+  for (int i = 0; i < n; ++i) {
     if ((sel >> i) & 1u) {
       const int e = e0 + i;
       const double s = (double)sigmoid_exact(load_logit<BF16>(a.logits, row + e));
       a.out_ids[(size_t)t * a.k + pos] = e;
       a.out_w[(size_t)t * a.k + pos] = (float)(s / ssum);
       atomicOr(&L.bits[e], 1ull << tl);
-      if (ids_cache) ids_cache[tl * a.k + pos] = e;
+      ids_cache[tl * a.k + pos] = e;
       ++pos;
     }
   }
+  __syncthreads();
 }
 
 // ----------------------------------------------------------------------------
-// Fast certified selection of one token by one wave.  Layout: E % 64 == 0 and
-// n_group divides 64; lane l owns the contiguous experts [l*epl, (l+1)*epl),
-// so group g is owned by the 64/n_group consecutive lanes starting at
-// g*64/n_group.  Returns false when the token must be decided exactly.
+// Selection of one token by one wave (see the header comment).  Layout:
+// E % 64 == 0, n_group divides 64.  `exact` recomputes every key with the
+// correctly rounded sigmoid (used when the group boundary is too close).
 // ----------------------------------------------------------------------------
-template <int EPLM, bool BF16>
-__device__ bool fast_token(const Args& a, const Lds& L, int t, int tl, double delta, double epsg,
-                           int* ids_cache) {
+template <int EPLM, bool BF16, int MODE>
+__device__ int wave_token(const Args& a, const Lds& L, int t, int tl, const float* bv, double delta,
+                          double epsg, bool exact, int* ids_cache) {
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  const int epl = a.E >> 6;
-  const int lpg = kWave / a.n_group;
+  const int epl = a.epl;
   const int e0 = lane * epl;
   const size_t row = (size_t)t * a.E;
+  constexpr int SZ = BF16 ? 2 : 4;
+  unsigned char* stage = L.stage + (size_t)w * L.stage_bytes;
 
-  // keys from the fast sigmoid; lane-local top-2
+  // ---- 1. load the row, keys, lane top-2 ----
   float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
+  auto put = [&](int i, float x) {
+    const float b = (EPLM <= kBiasRegMax) ? bv[i] : a.bias[e0 + i];
+    const float key = (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + b;
+    av[i] = key;
+    l2 = fmaxf(l2, fminf(lm, key));
+    lm = fmaxf(lm, key);
+  };
 #pragma unroll
-  for (int i = 0; i < EPLM; ++i) {
-    av[i] = -INFINITY;
-    if (i < epl) {
-      const float x = load_logit<BF16>(a.logits, row + e0 + i);
-      const float key = sigmoid_fast(x) + a.bias[e0 + i];
-      av[i] = key;
-      l2 = fmaxf(l2, fminf(lm, key));
-      lm = fmaxf(lm, key);
+  for (int i = 0; i < EPLM; ++i) av[i] = -INFINITY;
+  if constexpr (MODE == LOAD_STAGE) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
+                                                     row * SZ);
+    uint4* dst = reinterpret_cast<uint4*>(stage);
+    const int chunks = (a.E * SZ) >> 4;
+    for (int c = lane; c < chunks; c += kWave) dst[c] = src[c];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (BF16) {
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
+#pragma unroll
+      for (int i = 0; i < EPLM; ++i)
+        if (i < epl) put(i, __uint_as_float((uint32_t)s16[i] << 16));
+    } else {
+      const float* s32 = reinterpret_cast<const float*>(stage) + e0;
+#pragma unroll
+      for (int i = 0; i < EPLM; ++i)
+        if (i < epl) put(i, s32[i]);
+    }
+  } else {  // lane run is 16-byte aligned and a multiple of 16 bytes
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
+                                                     (row + e0) * SZ);
+    constexpr int PER = 16 / SZ;
+    static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
+#pragma unroll
+    for (int q = 0; q < (EPLM >= PER ? EPLM / PER : 0); ++q) {
+      if (q * PER < epl) {
+        const uint4 v = src[q];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (BF16) {
+            put(q * PER + 2 * j, __uint_as_float(d[j] << 16));
+            put(q * PER + 2 * j + 1, __uint_as_float(d[j] & 0xFFFF0000u));
+          } else {
+            put(q * PER + j, __uint_as_float(d[j]));
+          }
+        }
+      }
     }
   }
 
+  // ---- 2. group stage ----
   bool allowed = true;
   if (a.gstage) {
-    // group top-2 over the lpg lanes of the group, then group score
     float g1 = lm, g2 = l2;
-    for (int d = 1; d < lpg; d <<= 1) {
-      const float p1 = __shfl_xor(g1, d);
-      const float p2 = __shfl_xor(g2, d);
+    for (int lev = 0; (1 << lev) < a.lpg; ++lev) {
+      const float p1 = butterfly_partner(g1, lev);
+      const float p2 = butterfly_partner(g2, lev);
       const float n2 = fmaxf(fminf(g1, p1), fmaxf(g2, p2));
       g1 = fmaxf(g1, p1);
       g2 = n2;
     }
-    const float gs = g1 + g2;
-    const bool leader = (lane % lpg) == 0;
-    const uint32_t gsu = leader ? f2s(gs) : 0u;
-    const uint32_t aG = wave_kth(gsu, a.topk_group);
-    const uint32_t bG = wave_kth(gsu, a.topk_group + 1);
-    const double gap = (double)s2f(aG) - (double)s2f(bG);
-    if (!(gap > 2.0 * epsg)) return false;  // group boundary not certified
-    allowed = f2s(gs) >= aG;
+    const uint32_t gsu = f2s(g1 + g2);
+    const int g = lane / a.lpg;
+    const uint64_t cg = ((uint64_t)gsu << 32) | (uint32_t)(0xFFFFu - g);
+    int rank = 0;
+    for (int h = 0; h < a.n_group; ++h) {
+      const uint64_t ch = ((uint64_t)readlane(gsu, h * a.lpg) << 32) | (uint32_t)(0xFFFFu - h);
+      rank += ch > cg ? 1 : 0;
+    }
+    if (!exact) {
+      const int la = __builtin_ctzll(__ballot(rank == a.topk_group - 1));
+      const int lb = __builtin_ctzll(__ballot(rank == a.topk_group));
+      const double gap = (double)s2f(readlane(gsu, la)) - (double)s2f(readlane(gsu, lb));
+      if (!(gap > 2.0 * epsg)) return TOK_REDO_EXACT;  // boundary within the fast-key error
+    }
+    allowed = rank < a.topk_group;
   }
 
-  // candidate threshold: the k-th largest lane maximum among allowed lanes is
-  // a lower bound of the k-th largest key (k distinct lanes reach it)
-  if (__popcll(__ballot(allowed)) < a.k) return false;
-  const uint32_t tau0 = wave_kth(allowed ? f2s(lm) : 0u, a.k);
-  const float thr = next_down((float)((double)s2f(tau0) - 2.0 * delta));
-  unsigned long long cflags = 0;
+  // ---- 3. threshold: k-th largest lane maximum among allowed lanes ----
+  if (__popcll(__ballot(allowed)) < a.k) return TOK_ESCALATE;
+  const uint32_t ul = allowed ? f2s(lm) : 0u;
+  const uint32_t umax = wave_max_u32(ul);
+  const uint32_t umin = wave_min_u32(allowed ? ul : 0xFFFFFFFFu);
+  uint32_t T = umax;
+  if (umax != umin) {
+    const int top = 31 - __builtin_clz(umax ^ umin);
+    T = umax & ~((2u << top) - 1u);  // common prefix: every allowed lane maximum is >= T
+    const int lo = top > 15 ? top - 15 : 0;
+    for (int b = top; b >= lo; --b) {
+      const uint32_t c = T | (1u << b);
+      if (__popcll(__ballot(ul >= c)) >= a.k) T = c;  // keeps count(lane max >= T) >= k
+    }
+  }
+  float thr = s2f(T);
+  if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
+
+  // ---- 4. candidates, compacted in expert order ----
   int mine = 0;
+#pragma unroll
+  for (int i = 0; i < EPLM; ++i)
+    if (i < epl && allowed && av[i] >= thr) ++mine;
+  const int incl = wave_incl_scan(mine);
+  const int total = (int)readlane((uint32_t)incl, 63);
+  if (total > kCandMax) return TOK_ESCALATE;
+  int slot = incl - mine;
+  int* ci = L.cand_i + w * kCandMax;
+  unsigned long long* cc = L.cand_c + w * kCandMax;
 #pragma unroll
   for (int i = 0; i < EPLM; ++i) {
     if (i < epl && allowed && av[i] >= thr) {
-      cflags |= 1ull << i;
-      ++mine;
-    }
-  }
-  const int total = wave_sum_i(mine);
-  if (total > kWave) return false;
-  int slot = wave_incl_scan(mine) - mine;
-  float* ca_buf = L.cand_a + w * kWave;
-  int* ci_buf = L.cand_i + w * kWave;
-#pragma unroll
-  for (int i = 0; i < EPLM; ++i) {
-    if ((cflags >> i) & 1ull) {
-      ca_buf[slot] = av[i];
-      ci_buf[slot] = e0 + i;
+      ci[slot] = e0 + i;
       ++slot;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // one candidate per lane, in expert order
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- 5. exact keys of the candidates, exact ranks ----
   const bool has = lane < total;
-  const float ca = has ? ca_buf[lane] : -INFINITY;
-  const int ci = has ? ci_buf[lane] : 0;
-  __builtin_amdgcn_wave_barrier();
-  const uint32_t cu = has ? f2s(ca) : 0u;
-  const uint32_t kth = wave_kth(cu, a.k);
-  if (__popcll(__ballot(has && cu >= kth)) != a.k) return false;  // tie at the k-th key
-  if (total > a.k) {
-    const float nxt = wave_max_f((has && cu < kth) ? ca : -INFINITY);
-    const double gap = (double)s2f(kth) - (double)nxt;
-    if (!(gap > 2.0 * delta)) return false;  // k-th / (k+1)-th boundary not certified
+  const int ce = has ? ci[lane] : 0;
+  double s = 0.0;
+  unsigned long long mykey = 0ull;
+  if (has) {
+    float x;
+    if constexpr (MODE == LOAD_STAGE) {
+      if constexpr (BF16) x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(stage)[ce] << 16);
+      else x = reinterpret_cast<const float*>(stage)[ce];
+    } else {
+      x = load_logit<BF16>(a.logits, row + ce);
+    }
+    const float sf = sigmoid_exact(x);
+    s = (double)sf;
+    mykey = ((unsigned long long)f2s(sf + a.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
+    cc[lane] = mykey;
   }
-  // certified: the k lanes with key >= kth are the exact picks
-  const bool sel = has && cu >= kth;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+  for (int j = 0; j < total; ++j) rank += cc[j] > mykey ? 1 : 0;
+  const bool sel = has && rank < a.k;
+
+  // ---- 6. outputs in expert order, weights in float64 ----
   const unsigned long long selm = __ballot(sel);
   const int pos = __popcll(selm & ((1ull << lane) - 1ull));
-  double s = 0.0;
-  if (sel) s = (double)sigmoid_exact(load_logit<BF16>(a.logits, row + ci));
-  const double ssum = wave_sum_d(s);
+  const double ssum = wave_sum_d(sel ? s : 0.0);
   if (sel) {
-    a.out_ids[(size_t)t * a.k + pos] = ci;
+    a.out_ids[(size_t)t * a.k + pos] = ce;
     a.out_w[(size_t)t * a.k + pos] = (float)(s / ssum);
-    atomicOr(&L.bits[ci], 1ull << tl);
-    if (ids_cache) ids_cache[tl * a.k + pos] = ci;
+    atomicOr(&L.bits[ce], 1ull << tl);
+    ids_cache[tl * a.k + pos] = ce;
   }
-  return true;
+  __builtin_amdgcn_wave_barrier();
+  return TOK_DONE;
 }
 
-// Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets.
-template <int EPLM, bool BF16>
-__device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt, int* ids_cache) {
+// Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets
+// and the per-token expert lists in LDS.
+template <int EPLM, bool BF16, int MODE>
+__device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   const int tid = threadIdx.x;
   for (int e = tid; e < a.E; e += kWG) L.bits[e] = 0ull;
   if (tid == 0) L.misc[0] = 0;
-  float bm = 0.0f;
-  for (int e = tid; e < a.E; e += kWG) bm = fmaxf(bm, fabsf(a.bias[e]));
-  bm = wg_max_f(L, bm);  // contains barriers
   // |fast key - exact key| <= 2^-21 + (rounding of both sums) <= delta;
   // |fast group score - exact group score| <= 2*delta + rounding <= epsg
+  uint32_t bmax = 0;
+  for (int e = tid; e < a.E; e += kWG) bmax = max(bmax, __float_as_uint(fabsf(a.bias[e])));
+  const float bm = __uint_as_float(wg_max_u32(L, bmax));  // contains barriers
   const double B = 1.0 + (double)bm + 0x1p-20;  // bound on |key|
   const double delta = 0x1p-21 + (B + 1.0) * 0x1p-23;
   const double epsg = 2.0 * delta + (2.0 * B + 1.0) * 0x1p-23;
   if (a.fast) {
     const int w = tid >> 6;
-    for (int tl = w; tl < nt; tl += kNWaves) {
-      const bool ok = fast_token<EPLM, BF16>(a, L, t0 + tl, tl, delta, epsg, ids_cache);
-      if (!ok && lane_id() == 0) {
+    const int e0 = lane_id() * a.epl;
+    float bv[EPLM <= kBiasRegMax ? EPLM : 1];
+#pragma unroll
+    for (int i = 0; i < (EPLM <= kBiasRegMax ? EPLM : 0); ++i) bv[i] = i < a.epl ? a.bias[e0 + i] : 0.0f;
+    for (int tl = w; tl < nt; tl += kNW) {
+      int st = wave_token<EPLM, BF16, MODE>(a, L, t0 + tl, tl, bv, delta, epsg, false, L.ids);
+      if (st == TOK_REDO_EXACT)
+        st = wave_token<EPLM, BF16, MODE>(a, L, t0 + tl, tl, bv, delta, epsg, true, L.ids);
+      if (st == TOK_ESCALATE && lane_id() == 0) {
         const int q = atomicAdd(&L.misc[0], 1);
         L.esc[q] = tl;
       }
@@ -591,7 +706,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt, int* 
   const int nesc = L.misc[0];
   for (int q = 0; q < nesc; ++q) {
     const int tl = L.esc[q];
-    exact_token<BF16>(a, L, t0 + tl, tl, ids_cache);
+    exact_token_wg<BF16>(a, L, t0 + tl, tl, L.ids);
   }
   if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], nesc);
@@ -601,7 +716,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt, int* 
 }
 
 // Exclusive scan of padded counts over all experts into L.off; returns the
-// total (valid in every thread).  `padded(e)` gives expert e's padded count.
+// total (in every thread).  `padded(e)` gives expert e's padded count.
 template <typename F>
 __device__ int expert_offsets(const Args& a, const Lds& L, F padded) {
   const int tid = threadIdx.x;
@@ -634,10 +749,10 @@ __device__ int expert_offsets(const Args& a, const Lds& L, F padded) {
 // Kernels.
 // ----------------------------------------------------------------------------
 // Everything in one workgroup (M <= 64): one launch per call.
-template <int EPLM, bool BF16>
-__global__ __launch_bounds__(kWG) void k_small(Args a) {
-  const Lds L = carve(KIND_SMALL, a);
-  select_tokens<EPLM, BF16>(a, L, 0, a.M, L.ids);
+template <int EPLM, bool BF16, int MODE>
+__global__ __launch_bounds__(kWG) void k_small(Args a, int stage_bytes) {
+  const Lds L = carve(KIND_SMALL, a, stage_bytes);
+  select_tokens<EPLM, BF16, MODE>(a, L, 0, a.M);
   const int tid = threadIdx.x;
   const int total = expert_offsets(a, L, [&](int e) { return pad_up(__popcll(L.bits[e]), a.block); });
   if (tid == 0) *a.npp = total;
@@ -657,48 +772,63 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   }
 }
 
-// Multi-workgroup path, launch 1: selection and per-workgroup histograms.
-template <int EPLM, bool BF16>
-__global__ __launch_bounds__(kWG) void k_select(Args a) {
-  const Lds L = carve(KIND_SELECT, a);
+// Multi-workgroup path, launch 1: selection, per-workgroup histogram row and
+// one record (expert, rank inside the workgroup) per slot.
+template <int EPLM, bool BF16, int MODE>
+__global__ __launch_bounds__(kWG) void k_select(Args a, int stage_bytes) {
+  const Lds L = carve(KIND_SELECT, a, stage_bytes);
   const int w = blockIdx.x;
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
-  select_tokens<EPLM, BF16>(a, L, t0, nt, nullptr);
+  select_tokens<EPLM, BF16, MODE>(a, L, t0, nt);
   for (int e = threadIdx.x; e < a.E; e += kWG)
     a.ws_hist[(size_t)w * a.E + e] = __popcll(L.bits[e]);
+  const int ns = nt * a.k;
+  int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
+  for (int q = threadIdx.x; q < ns; q += kWG) {
+    const int tl = q / a.k;
+    const int e = L.ids[q];
+    rec[q] = e | (__popcll(L.bits[e] & ((1ull << tl) - 1ull)) << 16);
+  }
 }
 
-// Launch 2: per expert, exclusive scan of the histogram column in workgroup
-// order (in place) and the padded total.  64 experts x 4 row ranges per block.
+// Launch 2: per expert, exclusive scan of its histogram column in workgroup
+// order (in place) and the padded total.  A block covers 32 experts; each of
+// its 16 row ranges is summed, the sums are scanned across in LDS, and the
+// rows are rewritten as prefixes.
+constexpr int kColE = 32;
+constexpr int kColParts = kWG / kColE;
+
 __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
-  __shared__ int part[kNWaves][kWave];
-  const int ex = threadIdx.x & (kWave - 1);
-  const int pt = threadIdx.x >> 6;
-  const int e = blockIdx.x * kWave + ex;
-  const int chunk = (a.nwg + kNWaves - 1) / kNWaves;
-  const int w0 = pt * chunk;
+  __shared__ int part[kColParts][kColE];
+  const int ex = threadIdx.x % kColE;
+  const int pt = threadIdx.x / kColE;
+  const int e = blockIdx.x * kColE + ex;
+  const int chunk = (a.nwg + kColParts - 1) / kColParts;
+  const int w0 = min(a.nwg, pt * chunk);
   const int w1 = min(a.nwg, w0 + chunk);
   int s = 0;
-  if (e < a.E)
+  if (e < a.E) {
+#pragma unroll 8
     for (int w = w0; w < w1; ++w) s += a.ws_hist[(size_t)w * a.E + e];
+  }
   part[pt][ex] = s;
   __syncthreads();
   int pre = 0, total = 0;
-  for (int q = 0; q < kNWaves; ++q) {
+  for (int q = 0; q < kColParts; ++q) {
     if (q < pt) pre += part[q][ex];
     total += part[q][ex];
   }
   if (e < a.E) {
-    int run = pre;
+    int32_t* col = a.ws_hist + e;
+#pragma unroll 8
     for (int w = w0; w < w1; ++w) {
-      const size_t i = (size_t)w * a.E + e;
-      const int v = a.ws_hist[i];
-      a.ws_hist[i] = run;
-      run += v;
+      const int v = col[(size_t)w * a.E];
+      col[(size_t)w * a.E] = pre;
+      pre += v;
     }
     if (pt == 0) {
-      a.ws_cnt[e] = total;
+      a.ws_tot[e] = total;
       a.ws_pad[e] = pad_up(total, a.block);
     }
   }
@@ -706,41 +836,37 @@ __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
 
 // Launch 3: expert offsets, padding, expert_of_block and the stable scatter.
 __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
-  const Lds L = carve(KIND_SCATTER, a);
+  const Lds L = carve(KIND_SCATTER, a, 0);
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
-  for (int e = tid; e < a.E; e += kWG) L.bits[e] = 0ull;
   const int total = expert_offsets(a, L, [&](int e) { return a.ws_pad[e]; });
   if (w == 0 && tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
   const int es0 = (int)((int64_t)w * a.E / a.nwg);
   const int es1 = (int)((int64_t)(w + 1) * a.E / a.nwg);
   for (int e = es0; e < es1; ++e) {
-    const int c = a.ws_cnt[e];
+    const int c = a.ws_tot[e];
     const int p = a.ws_pad[e];
     const int o = L.off[e];
     for (int r = c + tid; r < p; r += kWG) a.sorted_ids[o + r] = sentinel;
     for (int b = tid; b < p / a.block; b += kWG) a.eob[o / a.block + b] = e;
   }
   const int ns = nt * a.k;
-  const int32_t* ids = a.out_ids + (size_t)t0 * a.k;
-  for (int q = tid; q < ns; q += kWG) atomicOr(&L.bits[ids[q]], 1ull << (q / a.k));
-  __syncthreads();
+  const int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
   const int32_t* colpre = a.ws_hist + (size_t)w * a.E;
   for (int q = tid; q < ns; q += kWG) {
-    const int tl = q / a.k;
-    const int e = ids[q];
-    const int rank = colpre[e] + __popcll(L.bits[e] & ((1ull << tl) - 1ull));
-    a.sorted_ids[L.off[e] + rank] = t0 * a.k + q;
+    const int r = rec[q];
+    const int e = r & 0xFFFF;
+    a.sorted_ids[L.off[e] + colpre[e] + (r >> 16)] = t0 * a.k + q;
   }
 }
 
 __global__ void k_zero_npp(int32_t* npp) { *npp = 0; }
 
-__global__ __launch_bounds__(kWG) void k_sigmoid_probe(const float* x, int n, float* f, float* e) {
-  const int i = blockIdx.x * kWG + threadIdx.x;
+__global__ __launch_bounds__(256) void k_sigmoid_probe(const float* x, int n, float* f, float* e) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) {
     f[i] = sigmoid_fast(x[i]);
     e[i] = sigmoid_exact(x[i]);
@@ -752,7 +878,7 @@ __global__ __launch_bounds__(kWG) void k_sigmoid_probe(const float* x, int n, fl
 // ----------------------------------------------------------------------------
 int choose_tw(int M) {
   int tw = (M + 511) / 512;
-  if (tw < 4) tw = 4;
+  if (tw < 1) tw = 1;
   if (tw > kTwMax) tw = kTwMax;
   return tw;
 }
@@ -763,15 +889,17 @@ bool valid_sizes(int M, int E, int k, int block) {
 
 int64_t max_rows_of(int M, int E, int k, int block) {
   const int64_t routes = (int64_t)M * k;
-  const int64_t r = routes + (routes < E ? routes : (int64_t)E) * (int64_t)(block - 1);
-  return r;
+  return routes + (routes < E ? routes : (int64_t)E) * (int64_t)(block - 1);
 }
 
-size_t workspace_of(int M, int E) {
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+size_t workspace_of(int M, int E, int k) {
   if (M == 0) return 0;
   const int tw = choose_tw(M);
   const int64_t nwg = ((int64_t)M + tw - 1) / tw;
-  return kWsHeader + (size_t)2 * E * 4 + (size_t)nwg * E * 4;
+  return kWsHeader + align16((size_t)2 * E * 4) + align16((size_t)nwg * E * 4) +
+         align16((size_t)M * k * 4);
 }
 
 int eplm_bucket(int epl) {
@@ -780,28 +908,36 @@ int eplm_bucket(int epl) {
   return b;
 }
 
-typedef void (*KernelFn)(Args);
+typedef void (*KernelFn)(Args, int);
 
-#define MRS_PICK(KER)                                                                 \
-  KernelFn pick_##KER(int eplm, bool bf16) {                                          \
-    switch (eplm) {                                                                   \
-      case 1: return bf16 ? KER<1, true> : KER<1, false>;                             \
-      case 2: return bf16 ? KER<2, true> : KER<2, false>;                             \
-      case 4: return bf16 ? KER<4, true> : KER<4, false>;                             \
-      case 8: return bf16 ? KER<8, true> : KER<8, false>;                             \
-      case 16: return bf16 ? KER<16, true> : KER<16, false>;                          \
-      case 32: return bf16 ? KER<32, true> : KER<32, false>;                          \
-      default: return bf16 ? KER<64, true> : KER<64, false>;                          \
-    }                                                                                 \
+#define MRS_PICK(KER)                                                                        \
+  template <bool BF16, int MODE>                                                             \
+  KernelFn pick2_##KER(int eplm) {                                                           \
+    switch (eplm) {                                                                          \
+      case 1: return KER<1, BF16, MODE>;                                                     \
+      case 2: return KER<2, BF16, MODE>;                                                     \
+      case 4: return KER<4, BF16, MODE>;                                                     \
+      case 8: return KER<8, BF16, MODE>;                                                     \
+      case 16: return KER<16, BF16, MODE>;                                                   \
+      case 32: return KER<32, BF16, MODE>;                                                   \
+      default: return KER<64, BF16, MODE>;                                                   \
+    }                                                                                        \
+  }                                                                                          \
+  KernelFn pick_##KER(int eplm, bool bf16, int mode) {                                       \
+    if (bf16) return mode == LOAD_VEC ? pick2_##KER<true, LOAD_VEC>(eplm)                    \
+                                      : pick2_##KER<true, LOAD_STAGE>(eplm);                 \
+    return mode == LOAD_VEC ? pick2_##KER<false, LOAD_VEC>(eplm)                             \
+                            : pick2_##KER<false, LOAD_STAGE>(eplm);                          \
   }
 MRS_PICK(k_small)
 MRS_PICK(k_select)
 #undef MRS_PICK
 
-int launch(KernelFn fn, int grid, size_t lds, hipStream_t stream, Args* a) {
-  void* params[] = {a};
-  const hipError_t err =
-      hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kWG), params, lds, stream);
+int launch(const void* fn, int grid, size_t lds, hipStream_t stream, void** params) {
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return MRS_ERR_LAUNCH;
+  const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kWG), params, lds, stream);
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 
@@ -840,7 +976,7 @@ int64_t moe_route_sort_max_blocks(int M, int E, int k, int block) {
 
 size_t moe_route_sort_workspace_bytes(int M, int E, int k, int block) {
   if (!valid_sizes(M, E, k, block)) return (size_t)-1;
-  return workspace_of(M, E);
+  return workspace_of(M, E, k);
 }
 
 int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,
@@ -883,6 +1019,8 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   a.G = E / n_group;
   a.gstage = (n_group > 1 && topk_group < n_group && a.G > 1) ? 1 : 0;
   a.fast = (E % kWave == 0 && kWave % n_group == 0 && !(flags & MRS_FLAG_FORCE_EXACT)) ? 1 : 0;
+  a.epl = E / kWave;
+  a.lpg = kWave / n_group;
   a.out_ids = out_ids;
   a.out_w = out_w;
   a.sorted_ids = sorted_ids;
@@ -890,34 +1028,46 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   a.npp = num_post_pad;
   a.stats = stats;
   const bool bf16 = logits_dtype == MRS_DTYPE_BF16;
-  const int eplm = a.fast ? eplm_bucket(E / kWave) : 1;
+  const int sz = bf16 ? 2 : 4;
+  const int eplm = a.fast ? eplm_bucket(a.epl) : 1;
+  // lane runs that are whole 16-byte vectors load straight from HBM; others
+  // go through a per-wave LDS copy of the row
+  const int mode = (a.fast && (a.epl * sz) % 16 == 0) ? LOAD_VEC : LOAD_STAGE;
+  int stage_bytes = (a.fast && mode == LOAD_STAGE) ? E * sz : 0;
 
-  const bool small_fits = M <= kTwMax && (int64_t)M * k <= kSmallSlotsMax &&
-                          lds_plan(KIND_SMALL, E, n_group, a.gstage, M, k).total <= kLdsLimit;
-  bool small = small_fits && !(flags & MRS_FLAG_FORCE_MULTI_WG);
+  const bool small_fits = M <= kTwMax &&
+                          lds_plan(KIND_SMALL, E, n_group, a.gstage, a.fast, stage_bytes, M, k).total <= kLdsLimit;
+  const bool small = small_fits && !(flags & MRS_FLAG_FORCE_MULTI_WG);
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && !small_fits) return MRS_ERR_INVALID_ARG;
   if (small) {
     a.tw = M;
     a.nwg = 1;
-    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, a.tw, k).total;
-    return launch(pick_k_small(eplm, bf16), 1, lds, st, &a);
+    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, a.fast, stage_bytes, a.tw, k).total;
+    void* params[] = {&a, &stage_bytes};
+    return launch(reinterpret_cast<const void*>(pick_k_small(eplm, bf16, mode)), 1, lds, st, params);
   }
 
   a.tw = choose_tw(M);
   a.nwg = (M + a.tw - 1) / a.tw;
-  const size_t need = workspace_of(M, E);
+  const size_t need = workspace_of(M, E, k);
   if (workspace == nullptr || workspace_bytes < need) return MRS_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MRS_ERR_MISALIGNED;
-  int32_t* ws = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(workspace) + kWsHeader);
-  a.ws_cnt = ws;
-  a.ws_pad = ws + E;
-  a.ws_hist = ws + 2 * E;
-  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, a.tw, k).total;
-  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, a.tw, k).total;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace) + kWsHeader;
+  a.ws_tot = reinterpret_cast<int32_t*>(ws);
+  a.ws_pad = a.ws_tot + E;
+  ws += align16((size_t)2 * E * 4);
+  a.ws_hist = reinterpret_cast<int32_t*>(ws);
+  ws += align16((size_t)a.nwg * E * 4);
+  a.ws_slot = reinterpret_cast<int32_t*>(ws);
+  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, a.fast, stage_bytes, a.tw, k).total;
+  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, a.fast, 0, a.tw, k).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
-  int rc = launch(pick_k_select(eplm, bf16), a.nwg, lds_sel, st, &a);
-  if (rc == MRS_OK) rc = launch(k_colscan, (E + kWave - 1) / kWave, 0, st, &a);
-  if (rc == MRS_OK) rc = launch(k_scatter, a.nwg, lds_sct, st, &a);
+  void* p_sel[] = {&a, &stage_bytes};
+  void* p_one[] = {&a};
+  int rc = launch(reinterpret_cast<const void*>(pick_k_select(eplm, bf16, mode)), a.nwg, lds_sel, st, p_sel);
+  if (rc == MRS_OK)
+    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, 0, st, p_one);
+  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, lds_sct, st, p_one);
   return rc;
 }
 
@@ -938,8 +1088,8 @@ int moe_route_sort_sigmoid_probe(const float* x, int n, float* fast_out, float* 
   if (!aligned(x, 4) || !aligned(fast_out, 4) || !aligned(exact_out, 4)) return MRS_ERR_MISALIGNED;
   void* params[] = {&x, &n, &fast_out, &exact_out};
   const hipError_t err =
-      hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_probe), dim3((n + kWG - 1) / kWG),
-                      dim3(kWG), params, 0, reinterpret_cast<hipStream_t>(stream));
+      hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_probe), dim3((n + 255) / 256), dim3(256),
+                      params, 0, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 

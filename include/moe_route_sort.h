@@ -97,18 +97,18 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
 /* Option bits for moe_route_sort_ex (path selection for tests and tuning;
  * every path computes the same result). */
 enum {
-  MRS_FLAG_FORCE_SINGLE_WG = 1u << 0, /* one workgroup does everything (M*k <= 2048, M <= 64) */
+  MRS_FLAG_FORCE_SINGLE_WG = 1u << 0, /* one workgroup does everything (M <= 64)           */
   MRS_FLAG_FORCE_MULTI_WG = 1u << 1,  /* many workgroups, even for small M                  */
-  MRS_FLAG_FORCE_EXACT = 1u << 2      /* skip the fast certified selection; every token     */
-                                      /* takes the exact workgroup-wide selection           */
+  MRS_FLAG_FORCE_EXACT = 1u << 2      /* skip the one-wave selection; every token takes the */
+                                      /* exact workgroup-wide selection                     */
 };
 
 /*
  * moe_route_sort_ex -- moe_route_sort with option bits and optional device
  * statistics.  `stats`, when not NULL, is device int32[2] that the call
- * increments: stats[0] += tokens that took the exact workgroup-wide selection,
- * stats[1] += tokens selected by the fast certified path.  Unknown flag bits
- * or a forced path that cannot take the shape return MRS_ERR_INVALID_ARG.
+ * increments: stats[0] += tokens decided by the workgroup-wide exact selection,
+ * stats[1] += tokens decided by one wave.  Unknown flag bits or a forced path
+ * that cannot take the shape return MRS_ERR_INVALID_ARG.
  */
 int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,
                       int topk_group, int block, int32_t* out_ids, float* out_w,
