@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_route_sort.h"
 
 namespace {
@@ -51,7 +53,6 @@ constexpr int kEMax = 4096;              // 16 KiB of 32-bit counters, the pages
 constexpr int kBiasRegMax = 16;          // lanes keep their biases in registers up to this many experts
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kWsHeader = 256;
-constexpr int kCandMax = kWave;          // candidates per token in the wave path
 
 enum { KIND_SMALL = 0, KIND_SELECT = 1, KIND_SCATTER = 2 };
 enum { LOAD_VEC = 0, LOAD_STAGE = 1 };
@@ -62,8 +63,10 @@ struct Args {
   const float* bias;
   int M, E, k, n_group, topk_group, block;
   int G;       // experts per group
-  int epl;     // experts per lane in the wave path (E / 64)
-  int lpg;     // lanes per group in the wave path (64 / n_group)
+  int seg;    // lanes per token in the wave path (32 or 64)
+  int epl;     // experts per lane in the wave path (E / seg)
+  int nbuf;    // LDS row buffers per segment (2 when a wave takes several rounds)
+  int stage_bytes;  // bytes of one staged logits row (0: rows are read straight from HBM)
   int tw;      // tokens per workgroup
   int nwg;     // workgroups of the multi-workgroup path
   int fast;    // the wave layout covers this shape
@@ -84,11 +87,15 @@ struct Args {
 // LDS plan shared by host (size) and device (carving).
 // ----------------------------------------------------------------------------
 struct LdsPlan {
-  size_t bits, redd, off, ids, cand_i, cand_c, u, stage, ukey, grp, esc, misc, red, scan, total;
+  size_t bits, redd, off, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
-__host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gstage, int fast,
-                                            int stage_bytes, int tw, int k) {
+__host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes) {
+  return fast ? (size_t)kNW * nbuf * (kWave / seg) * stage_bytes : 0;
+}
+
+__host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gstage, size_t stage,
+                                            int tw, int k) {
   LdsPlan p{};
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
@@ -97,10 +104,12 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
   if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
   if (kind != KIND_SCATTER) {
     p.ids = take((size_t)tw * k * 4);
-    p.cand_c = take((size_t)kNW * kCandMax * 8);
-    p.cand_i = take((size_t)kNW * kCandMax * 4);
-    // union: wave staging buffers (fast loop) / exact keys + group arrays (after it)
-    const size_t stage = fast ? (size_t)kNW * stage_bytes : 0;
+    p.bias = take((size_t)E * 4);
+    p.cand_i = take((size_t)kNW * kWave * 4);
+    p.cand_c = take((size_t)kNW * kWave * 8);
+    p.gcomp = take((size_t)kNW * kWave * 8);
+    if (o < 1024) o = 1024;  // staging buffers start past 1 KiB (see stage_rows_async)
+    // union: wave staging buffers (wave loop) / exact keys + group arrays (after it)
     const size_t ex = (size_t)E * 4 + (gstage ? (size_t)3 * n_group * 4 + 16 : 0);
     const size_t un = stage > ex ? stage : ex;
     p.u = take(un);
@@ -121,8 +130,10 @@ struct Lds {
   double* redd;
   int* off;
   int* ids;
-  unsigned long long* cand_c;
+  float* bias;
   int* cand_i;
+  unsigned long long* cand_c;
+  unsigned long long* gcomp;
   unsigned char* stage;
   uint32_t* ukey;
   unsigned* grp;
@@ -130,20 +141,22 @@ struct Lds {
   int* misc;
   int* red;
   int* scan;
-  int stage_bytes;
 };
 
 extern __shared__ __align__(16) unsigned char g_lds[];
 
-__device__ inline Lds carve(int kind, const Args& a, int stage_bytes) {
-  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, a.fast, stage_bytes, a.tw, a.k);
+__device__ inline Lds carve(int kind, const Args& a) {
+  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes),
+                             a.tw, a.k);
   Lds L;
   L.bits = reinterpret_cast<unsigned long long*>(g_lds + p.bits);
   L.redd = reinterpret_cast<double*>(g_lds + p.redd);
   L.off = reinterpret_cast<int*>(g_lds + p.off);
   L.ids = reinterpret_cast<int*>(g_lds + p.ids);
-  L.cand_c = reinterpret_cast<unsigned long long*>(g_lds + p.cand_c);
+  L.bias = reinterpret_cast<float*>(g_lds + p.bias);
   L.cand_i = reinterpret_cast<int*>(g_lds + p.cand_i);
+  L.cand_c = reinterpret_cast<unsigned long long*>(g_lds + p.cand_c);
+  L.gcomp = reinterpret_cast<unsigned long long*>(g_lds + p.gcomp);
   L.stage = g_lds + p.stage;
   L.ukey = reinterpret_cast<uint32_t*>(g_lds + p.ukey);
   L.grp = reinterpret_cast<unsigned*>(g_lds + p.grp);
@@ -151,7 +164,6 @@ __device__ inline Lds carve(int kind, const Args& a, int stage_bytes) {
   L.misc = reinterpret_cast<int*>(g_lds + p.misc);
   L.red = reinterpret_cast<int*>(g_lds + p.red);
   L.scan = reinterpret_cast<int*>(g_lds + p.scan);
-  L.stage_bytes = stage_bytes;
   return L;
 }
 
@@ -330,17 +342,6 @@ __device__ double wg_sum_d(const Lds& L, double v) {
   return s;
 }
 
-__device__ uint32_t wg_max_u32(const Lds& L, uint32_t v) {
-  const int w = threadIdx.x >> 6;
-  v = wave_max_u32(v);
-  if (lane_id() == 0) L.red[w] = (int)v;
-  __syncthreads();
-  uint32_t m = 0;
-  for (int q = 0; q < kNW; ++q) m = max(m, (uint32_t)L.red[q]);
-  __syncthreads();
-  return m;
-}
-
 // Number of selected entries >= c among arr[i0 + i] (i < n, bit i of mask).
 __device__ __forceinline__ int wg_count_ge(const Lds& L, const uint32_t* arr, int i0, int n, uint32_t mask,
                                            uint32_t c, int parity) {
@@ -491,70 +492,174 @@ __device__ void exact_token_wg(const Args& a, const Lds& L, int t, int tl, int* 
 }
 
 // ----------------------------------------------------------------------------
-// Selection of one token by one wave (see the header comment).  Layout:
-// E % 64 == 0, n_group divides 64.  `exact` recomputes every key with the
-// correctly rounded sigmoid (used when the group boundary is too close).
+// Selection by wave segments (see the header comment).  A wave works on
+// NSEG = 64 / SEG tokens at once, one per segment of SEG consecutive lanes;
+// every per-token step (reductions, scans, ballot counts, rank counts) stays
+// inside its segment, so a wave pays the per-token control work once for
+// NSEG tokens.  Layout: E % SEG == 0, n_group divides SEG, lane l of a segment
+// owns experts [l*epl, (l+1)*epl) with epl = E / SEG.  EPL > 0 fixes epl at
+// compile time; EPL == 0 reads it from the arguments (up to 64).
 // ----------------------------------------------------------------------------
-template <int EPLM, bool BF16, int MODE>
-__device__ int wave_token(const Args& a, const Lds& L, int t, int tl, const float* bv, double delta,
-                          double epsg, bool exact, int* ids_cache) {
+// s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copy the rows of the tokens of a wave (one per segment, token < 0 = none)
+// from HBM into per-segment LDS buffers with gfx950's global_load_lds_dwordx4
+// (no VGPRs in flight).  Lane l writes LDS at base + 16*l, so the base for a
+// segment's instruction is shifted back by its first lane.
+template <int SEG>
+__device__ __forceinline__ void stage_rows_async(const Args& a, unsigned char* buf, int stage_bytes, int tok,
+                                                 int sz) {
+  constexpr int NSEG = kWave / SEG;
+  const int lane = lane_id();
+  const int seg = lane / SEG;
+  const int ls = lane % SEG;
+  const int chunks = (a.E * sz) >> 4;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.logits) + (size_t)(tok < 0 ? 0 : tok) * a.E * sz;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    unsigned char* dst = buf + (size_t)s * stage_bytes - (size_t)s * SEG * 16;  // >= 0: buffers start past 1 KiB
+    for (int j = 0; j * SEG < chunks; ++j) {
+      const int c = j * SEG + ls;
+      if (seg == s && tok >= 0 && c < chunks)
+        __builtin_amdgcn_global_load_lds(src + (size_t)c * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + j * SEG * 16), 16, 0, 0);
+    }
+  }
+}
+
+// Segment-local reductions and scans: DPP row shifts inside 16-lane rows,
+// then row broadcasts that join rows 0-1 and 2-3 (and, for 64-lane segments,
+// the two halves).  The result of a reduction is returned in every lane.
+template <int SEG>
+__device__ __forceinline__ uint32_t seg_bcast(uint32_t u) {
+  if constexpr (SEG == 64) return readlane(u, 63);
+  const uint32_t lo = readlane(u, 31), hi = readlane(u, 63);
+  return lane_id() < 32 ? lo : hi;
+}
+template <int SEG>
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t u) {
+  u = max(u, dpp<kRowShr1>(0u, u));
+  u = max(u, dpp<kRowShr2>(0u, u));
+  u = max(u, dpp<kRowShr4>(0u, u));
+  u = max(u, dpp<kRowShr8>(0u, u));
+  u = max(u, dpp<kRowBcast15, 0xA>(0u, u));
+  if constexpr (SEG == 64) u = max(u, dpp<kRowBcast31, 0xC>(0u, u));
+  return seg_bcast<SEG>(u);
+}
+template <int SEG>
+__device__ __forceinline__ uint32_t seg_min_u32(uint32_t u) {
+  u = min(u, dpp<kRowShr1>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr2>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr4>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowShr8>(0xFFFFFFFFu, u));
+  u = min(u, dpp<kRowBcast15, 0xA>(0xFFFFFFFFu, u));
+  if constexpr (SEG == 64) u = min(u, dpp<kRowBcast31, 0xC>(0xFFFFFFFFu, u));
+  return seg_bcast<SEG>(u);
+}
+template <int SEG>
+__device__ __forceinline__ int seg_incl_scan(int v) {
+  uint32_t u = (uint32_t)v;
+  u += dpp<kRowShr1>(0u, u);
+  u += dpp<kRowShr2>(0u, u);
+  u += dpp<kRowShr4>(0u, u);
+  u += dpp<kRowShr8>(0u, u);
+  u += dpp<kRowBcast15, 0xA>(0u, u);
+  if constexpr (SEG == 64) u += dpp<kRowBcast31, 0xC>(0u, u);
+  return (int)u;
+}
+template <int SEG>
+__device__ __forceinline__ double seg_sum_d(double v) {
+  auto step = [](double x, auto sh) {
+    const uint64_t b = __double_as_longlong(x);
+    const uint32_t lo = sh((uint32_t)b), hi = sh((uint32_t)(b >> 32));
+    return x + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  v = step(v, [](uint32_t u) { return dpp<kRowShr1>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr2>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr4>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowShr8>(0u, u); });
+  v = step(v, [](uint32_t u) { return dpp<kRowBcast15, 0xA>(0u, u); });
+  if constexpr (SEG == 64) v = step(v, [](uint32_t u) { return dpp<kRowBcast31, 0xC>(0u, u); });
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = seg_bcast<SEG>((uint32_t)b), hi = seg_bcast<SEG>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Bits of a ballot that belong to segment s, shifted down to bit 0.
+template <int SEG>
+__device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, int s) {
+  if constexpr (SEG == 64) return bal;
+  return (bal >> (s * SEG)) & 0xFFFFFFFFull;
+}
+
+template <int SEG, int EPL, bool BF16, int MODE>
+__device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, int t, int tl,
+                                         const unsigned char* stage, const float* bv, double delta,
+                                         double epsg, bool exact) {
+  constexpr int NSEG = kWave / SEG;
+  constexpr int EPLM = EPL > 0 ? EPL : 64;
+  using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  const int epl = a.epl;
-  const int e0 = lane * epl;
-  const size_t row = (size_t)t * a.E;
+  const int seg = lane / SEG;
+  const int ls = lane % SEG;
+  const int epl = EPL > 0 ? EPL : a.epl;
+  const int e0 = ls * epl;
+  const size_t row = (size_t)(act ? t : 0) * a.E;
   constexpr int SZ = BF16 ? 2 : 4;
-  unsigned char* stage = L.stage + (size_t)w * L.stage_bytes;
+  const unsigned long long below = (SEG == 64) ? ((1ull << lane) - 1ull) : ((1ull << ls) - 1ull);
+  int status = act ? TOK_DONE : TOK_ESCALATE;  // an idle segment writes nothing
 
-  // ---- 1. load the row, keys, lane top-2 ----
+  // ---- 1. keys and lane top-2 ----
   float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
+  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.bias[e0 + i]; };
   auto put = [&](int i, float x) {
-    const float b = (EPLM <= kBiasRegMax) ? bv[i] : a.bias[e0 + i];
-    const float key = (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + b;
+    const float key = (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i);
     av[i] = key;
     l2 = fmaxf(l2, fminf(lm, key));
     lm = fmaxf(lm, key);
+    if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
   };
 #pragma unroll
   for (int i = 0; i < EPLM; ++i) av[i] = -INFINITY;
-  if constexpr (MODE == LOAD_STAGE) {
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                     row * SZ);
-    uint4* dst = reinterpret_cast<uint4*>(stage);
-    const int chunks = (a.E * SZ) >> 4;
-    for (int c = lane; c < chunks; c += kWave) dst[c] = src[c];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if constexpr (BF16) {
-      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
+  if (act) {
+    if constexpr (MODE == LOAD_STAGE) {  // the row is already in this segment's LDS buffer
+      if constexpr (BF16) {
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
 #pragma unroll
-      for (int i = 0; i < EPLM; ++i)
-        if (i < epl) put(i, __uint_as_float((uint32_t)s16[i] << 16));
-    } else {
-      const float* s32 = reinterpret_cast<const float*>(stage) + e0;
+        for (int i = 0; i < EPLM; ++i)
+          if (i < epl) put(i, __uint_as_float((uint32_t)s16[i] << 16));
+      } else {
+        const float* s32 = reinterpret_cast<const float*>(stage) + e0;
 #pragma unroll
-      for (int i = 0; i < EPLM; ++i)
-        if (i < epl) put(i, s32[i]);
-    }
-  } else {  // lane run is 16-byte aligned and a multiple of 16 bytes
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                     (row + e0) * SZ);
-    constexpr int PER = 16 / SZ;
-    static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
+        for (int i = 0; i < EPLM; ++i)
+          if (i < epl) put(i, s32[i]);
+      }
+    } else {  // lane run is 16-byte aligned and a multiple of 16 bytes
+      constexpr int PER = 16 / SZ;
+      static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
+                                                       (row + e0) * SZ);
 #pragma unroll
-    for (int q = 0; q < (EPLM >= PER ? EPLM / PER : 0); ++q) {
-      if (q * PER < epl) {
-        const uint4 v = src[q];
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < (EPLM >= PER ? EPLM / PER : 0); ++q) {
+        if (q * PER < epl) {
+          const uint4 v = src[q];
+          const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (BF16) {
-            put(q * PER + 2 * j, __uint_as_float(d[j] << 16));
-            put(q * PER + 2 * j + 1, __uint_as_float(d[j] & 0xFFFF0000u));
-          } else {
-            put(q * PER + j, __uint_as_float(d[j]));
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (BF16) {
+              put(q * PER + 2 * j, __uint_as_float(d[j] << 16));
+              put(q * PER + 2 * j + 1, __uint_as_float(d[j] & 0xFFFF0000u));
+            } else {
+              put(q * PER + j, __uint_as_float(d[j]));
+            }
           }
         }
       }
@@ -562,10 +667,11 @@ __device__ int wave_token(const Args& a, const Lds& L, int t, int tl, const floa
   }
 
   // ---- 2. group stage ----
-  bool allowed = true;
+  bool allowed = act;
   if (a.gstage) {
+    const int lpg = SEG / a.n_group;
     float g1 = lm, g2 = l2;
-    for (int lev = 0; (1 << lev) < a.lpg; ++lev) {
+    for (int lev = 0; (1 << lev) < lpg; ++lev) {
       const float p1 = butterfly_partner(g1, lev);
       const float p2 = butterfly_partner(g2, lev);
       const float n2 = fmaxf(fminf(g1, p1), fmaxf(g2, p2));
@@ -573,67 +679,91 @@ __device__ int wave_token(const Args& a, const Lds& L, int t, int tl, const floa
       g2 = n2;
     }
     const uint32_t gsu = f2s(g1 + g2);
-    const int g = lane / a.lpg;
-    const uint64_t cg = ((uint64_t)gsu << 32) | (uint32_t)(0xFFFFu - g);
+    const int g = ls / lpg;
+    const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
+    unsigned long long* gc = L.gcomp + w * kWave + seg * SEG;
+    if (ls % lpg == 0) gc[g] = cg;
+    wave_sync_lds();
     int rank = 0;
-    for (int h = 0; h < a.n_group; ++h) {
-      const uint64_t ch = ((uint64_t)readlane(gsu, h * a.lpg) << 32) | (uint32_t)(0xFFFFu - h);
-      rank += ch > cg ? 1 : 0;
-    }
+    for (int h = 0; h < a.n_group; ++h) rank += gc[h] > cg ? 1 : 0;
+    const bool keep = rank < a.topk_group;
     if (!exact) {
-      const int la = __builtin_ctzll(__ballot(rank == a.topk_group - 1));
-      const int lb = __builtin_ctzll(__ballot(rank == a.topk_group));
-      const double gap = (double)s2f(readlane(gsu, la)) - (double)s2f(readlane(gsu, lb));
-      if (!(gap > 2.0 * epsg)) return TOK_REDO_EXACT;  // boundary within the fast-key error
+      // the kept groups' lowest score must beat the others' highest by more
+      // than the error of two fast group scores
+      const uint32_t kept_min = seg_min_u32<SEG>(keep ? gsu : 0xFFFFFFFFu);
+      const uint32_t drop_max = seg_max_u32<SEG>(keep ? 0u : gsu);
+      const double gap = (double)s2f(kept_min) - (double)s2f(drop_max);
+      if (act && !(gap > 2.0 * epsg)) status = TOK_REDO_EXACT;
     }
-    allowed = rank < a.topk_group;
+    allowed = act && keep;
   }
 
-  // ---- 3. threshold: k-th largest lane maximum among allowed lanes ----
-  if (__popcll(__ballot(allowed)) < a.k) return TOK_ESCALATE;
-  const uint32_t ul = allowed ? f2s(lm) : 0u;
-  const uint32_t umax = wave_max_u32(ul);
-  const uint32_t umin = wave_min_u32(allowed ? ul : 0xFFFFFFFFu);
-  uint32_t T = umax;
-  if (umax != umin) {
-    const int top = 31 - __builtin_clz(umax ^ umin);
-    T = umax & ~((2u << top) - 1u);  // common prefix: every allowed lane maximum is >= T
-    const int lo = top > 15 ? top - 15 : 0;
-    for (int b = top; b >= lo; --b) {
-      const uint32_t c = T | (1u << b);
-      if (__popcll(__ballot(ul >= c)) >= a.k) T = c;  // keeps count(lane max >= T) >= k
+  // ---- 3. threshold: k-th largest of the kept lanes' two largest keys ----
+  // (at least k keys reach it, so every exact top-k key has A >= it - 2 delta)
+  constexpr int R = EPLM >= 2 ? 2 : 1;
+  const int nallow = (int)__popcll(seg_bits<SEG>(__ballot(allowed), seg));
+  if (status == TOK_DONE && nallow * (EPL == 1 || (EPL == 0 && epl < 2) ? 1 : R) < a.k) status = TOK_ESCALATE;
+  const bool two = R == 2 && (EPL > 0 || epl >= 2);
+  const uint32_t u1 = allowed ? f2s(lm) : 0u;
+  const uint32_t u2 = (allowed && two) ? f2s(l2) : 0u;
+  const uint32_t vmax = seg_max_u32<SEG>(u1);
+  const uint32_t vmin = seg_min_u32<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
+  uint32_t Ts[NSEG];
+  int tops[NSEG];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const uint32_t hi = readlane(vmax, s * SEG), lo = readlane(vmin, s * SEG);
+    tops[s] = (hi == lo || lo > hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
+    Ts[s] = tops[s] < 0 ? min(hi, lo) : (hi & ~((2u << tops[s]) - 1u));  // every value counted is >= Ts
+  }
+  constexpr int kSteps = 12;  // resolve the 12 highest differing bits
+  for (int j = 0; j < kSteps; ++j) {
+    uint32_t cs[NSEG];
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) cs[s] = (tops[s] - j >= 0) ? (Ts[s] | (1u << (tops[s] - j))) : Ts[s];
+    uint32_t c = cs[0];
+#pragma unroll
+    for (int s = 1; s < NSEG; ++s) c = seg == s ? cs[s] : c;
+    const unsigned long long m1 = __ballot(u1 >= c);
+    const unsigned long long m2 = __ballot(u2 >= c);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      const int n = (int)(__popcll(seg_bits<SEG>(m1, s)) + __popcll(seg_bits<SEG>(m2, s)));
+      if (n >= a.k) Ts[s] = cs[s];
     }
   }
+  uint32_t T = Ts[0];
+#pragma unroll
+  for (int s = 1; s < NSEG; ++s) T = seg == s ? Ts[s] : T;
   float thr = s2f(T);
   if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
 
   // ---- 4. candidates, compacted in expert order ----
-  int mine = 0;
+  MaskT cm = 0;
 #pragma unroll
   for (int i = 0; i < EPLM; ++i)
-    if (i < epl && allowed && av[i] >= thr) ++mine;
-  const int incl = wave_incl_scan(mine);
-  const int total = (int)readlane((uint32_t)incl, 63);
-  if (total > kCandMax) return TOK_ESCALATE;
-  int slot = incl - mine;
-  int* ci = L.cand_i + w * kCandMax;
-  unsigned long long* cc = L.cand_c + w * kCandMax;
-#pragma unroll
-  for (int i = 0; i < EPLM; ++i) {
-    if (i < epl && allowed && av[i] >= thr) {
-      ci[slot] = e0 + i;
-      ++slot;
+    if (i < epl && av[i] >= thr) cm |= (MaskT)1 << i;
+  if (!allowed || status != TOK_DONE) cm = 0;
+  const int mine = (int)__popcll((unsigned long long)cm);
+  const int incl = seg_incl_scan<SEG>(mine);
+  const int total = (int)seg_bcast<SEG>((uint32_t)incl);
+  if (status == TOK_DONE && total > SEG) status = TOK_ESCALATE;
+  int* ci = L.cand_i + w * kWave + seg * SEG;
+  if (status == TOK_DONE) {
+    int slot = incl - mine;
+    while (cm) {
+      const int i = (int)__builtin_ctzll((unsigned long long)cm);
+      ci[slot++] = e0 + i;
+      cm &= cm - 1;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_sync_lds();
 
-  // ---- 5. exact keys of the candidates, exact ranks ----
-  const bool has = lane < total;
-  const int ce = has ? ci[lane] : 0;
+  // ---- 5. exact keys of the candidates, ranks by (key desc, index asc) ----
+  const bool has = status == TOK_DONE && ls < total;
+  const int ce = has ? ci[ls] : 0;
   double s = 0.0;
-  unsigned long long mykey = 0ull;
+  unsigned long long mykey = 0ull;  // below every real key
   if (has) {
     float x;
     if constexpr (MODE == LOAD_STAGE) {
@@ -644,56 +774,98 @@ __device__ int wave_token(const Args& a, const Lds& L, int t, int tl, const floa
     }
     const float sf = sigmoid_exact(x);
     s = (double)sf;
-    mykey = ((unsigned long long)f2s(sf + a.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
-    cc[lane] = mykey;
+    mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  unsigned long long* cc = L.cand_c + w * kWave + seg * SEG;
+  cc[ls] = mykey;
+  wave_sync_lds();
+  int tmax = (int)readlane((uint32_t)(status == TOK_DONE ? total : 0), 0);
+#pragma unroll
+  for (int q = 1; q < NSEG; ++q) tmax = max(tmax, (int)readlane((uint32_t)(status == TOK_DONE ? total : 0), q * SEG));
   int rank = 0;
-  for (int j = 0; j < total; ++j) rank += cc[j] > mykey ? 1 : 0;
+  for (int j = 0; j < tmax; j += 2) {
+    const unsigned long long c0 = cc[j], c1 = cc[j + 1];
+    rank += (c0 > mykey ? 1 : 0) + (c1 > mykey ? 1 : 0);
+  }
   const bool sel = has && rank < a.k;
 
   // ---- 6. outputs in expert order, weights in float64 ----
-  const unsigned long long selm = __ballot(sel);
-  const int pos = __popcll(selm & ((1ull << lane) - 1ull));
-  const double ssum = wave_sum_d(sel ? s : 0.0);
+  const int pos = (int)__popcll(seg_bits<SEG>(__ballot(sel), seg) & below);
+  const double ssum = seg_sum_d<SEG>(sel ? s : 0.0);
   if (sel) {
     a.out_ids[(size_t)t * a.k + pos] = ce;
     a.out_w[(size_t)t * a.k + pos] = (float)(s / ssum);
     atomicOr(&L.bits[ce], 1ull << tl);
-    ids_cache[tl * a.k + pos] = ce;
+    L.ids[tl * a.k + pos] = ce;
   }
-  __builtin_amdgcn_wave_barrier();
-  return TOK_DONE;
+  wave_sync_lds();
+  return status;
 }
 
 // Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets
-// and the per-token expert lists in LDS.
-template <int EPLM, bool BF16, int MODE>
+// and the per-token expert lists in LDS.  Wave w, round it takes tokens
+// (it*kNW + w)*NSEG + segment.
+template <int SEG, int EPL, bool BF16, int MODE>
 __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
+  constexpr int NSEG = kWave / SEG;
+  constexpr int EPLM = EPL > 0 ? EPL : 64;
   const int tid = threadIdx.x;
-  for (int e = tid; e < a.E; e += kWG) L.bits[e] = 0ull;
+  const int w = tid >> 6;
+  const int seg = lane_id() / SEG;
+  const int ls = lane_id() % SEG;
+  const int sb = a.stage_bytes;
+  unsigned char* stg = L.stage + (size_t)w * a.nbuf * NSEG * sb;
+  auto tok_of = [&](int it) { const int tl = (it * kNW + w) * NSEG + seg; return tl < nt ? tl : -1; };
+  if (a.fast && MODE == LOAD_STAGE) {
+    const int tl = tok_of(0);
+    stage_rows_async<SEG>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
+  }
+  for (int e = tid; e < a.E; e += kWG) {
+    L.bits[e] = 0ull;
+    L.bias[e] = a.bias[e];
+  }
   if (tid == 0) L.misc[0] = 0;
-  // |fast key - exact key| <= 2^-21 + (rounding of both sums) <= delta;
-  // |fast group score - exact group score| <= 2*delta + rounding <= epsg
-  uint32_t bmax = 0;
-  for (int e = tid; e < a.E; e += kWG) bmax = max(bmax, __float_as_uint(fabsf(a.bias[e])));
-  const float bm = __uint_as_float(wg_max_u32(L, bmax));  // contains barriers
-  const double B = 1.0 + (double)bm + 0x1p-20;  // bound on |key|
-  const double delta = 0x1p-21 + (B + 1.0) * 0x1p-23;
-  const double epsg = 2.0 * delta + (2.0 * B + 1.0) * 0x1p-23;
+  __syncthreads();
   if (a.fast) {
-    const int w = tid >> 6;
-    const int e0 = lane_id() * a.epl;
+    const int epl = EPL > 0 ? EPL : a.epl;
+    const int e0 = ls * epl;
     float bv[EPLM <= kBiasRegMax ? EPLM : 1];
+    float bmax = 0.0f;
+    if constexpr (EPLM <= kBiasRegMax) {
 #pragma unroll
-    for (int i = 0; i < (EPLM <= kBiasRegMax ? EPLM : 0); ++i) bv[i] = i < a.epl ? a.bias[e0 + i] : 0.0f;
-    for (int tl = w; tl < nt; tl += kNW) {
-      int st = wave_token<EPLM, BF16, MODE>(a, L, t0 + tl, tl, bv, delta, epsg, false, L.ids);
-      if (st == TOK_REDO_EXACT)
-        st = wave_token<EPLM, BF16, MODE>(a, L, t0 + tl, tl, bv, delta, epsg, true, L.ids);
-      if (st == TOK_ESCALATE && lane_id() == 0) {
+      for (int i = 0; i < EPLM; ++i) {
+        bv[i] = i < epl ? L.bias[e0 + i] : 0.0f;
+        bmax = fmaxf(bmax, fabsf(bv[i]));
+      }
+    } else {
+      for (int i = 0; i < epl; ++i) bmax = fmaxf(bmax, fabsf(L.bias[e0 + i]));
+    }
+    // Every segment covers all experts, so this is max |bias|.
+    // |fast key - exact key| <= 2^-21 + rounding of both sums <= delta;
+    // |fast group score - exact group score| <= 2*delta + rounding <= epsg
+    const double B = 1.0 + (double)__uint_as_float(wave_max_u32(__float_as_uint(bmax))) + 0x1p-20;
+    const double delta = 0x1p-21 + (B + 1.0) * 0x1p-23;
+    const double epsg = 2.0 * delta + (2.0 * B + 1.0) * 0x1p-23;
+    for (int it = 0; (it * kNW + w) * NSEG < nt; ++it) {
+      const int tl = tok_of(it);
+      const int cb = a.nbuf > 1 ? (it & 1) : 0;
+      const unsigned char* cur = stg + (size_t)(cb * NSEG + seg) * sb;
+      if (MODE == LOAD_STAGE) {
+        wait_vmem_all();  // this round's rows have landed in LDS
+        // the host gives two buffers whenever a wave has a next round
+        if (a.nbuf > 1 && ((it + 1) * kNW + w) * NSEG < nt) {
+          const int tn = tok_of(it + 1);
+          stage_rows_async<SEG>(a, stg + (size_t)(cb ^ 1) * NSEG * sb, sb, tn < 0 ? -1 : t0 + tn, BF16 ? 2 : 4);
+        }
+      }
+      const bool act = tl >= 0;
+      int st = seg_token<SEG, EPL, BF16, MODE>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
+      if (__ballot(act && st == TOK_REDO_EXACT)) {
+        const bool redo = act && st == TOK_REDO_EXACT;
+        const int st2 = seg_token<SEG, EPL, BF16, MODE>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
+        if (redo) st = st2;
+      }
+      if (act && st == TOK_ESCALATE && ls == 0) {
         const int q = atomicAdd(&L.misc[0], 1);
         L.esc[q] = tl;
       }
@@ -749,10 +921,10 @@ __device__ int expert_offsets(const Args& a, const Lds& L, F padded) {
 // Kernels.
 // ----------------------------------------------------------------------------
 // Everything in one workgroup (M <= 64): one launch per call.
-template <int EPLM, bool BF16, int MODE>
-__global__ __launch_bounds__(kWG) void k_small(Args a, int stage_bytes) {
-  const Lds L = carve(KIND_SMALL, a, stage_bytes);
-  select_tokens<EPLM, BF16, MODE>(a, L, 0, a.M);
+template <int SEG, int EPL, bool BF16, int MODE>
+__global__ __launch_bounds__(kWG) void k_small(Args a) {
+  const Lds L = carve(KIND_SMALL, a);
+  select_tokens<SEG, EPL, BF16, MODE>(a, L, 0, a.M);
   const int tid = threadIdx.x;
   const int total = expert_offsets(a, L, [&](int e) { return pad_up(__popcll(L.bits[e]), a.block); });
   if (tid == 0) *a.npp = total;
@@ -774,13 +946,13 @@ __global__ __launch_bounds__(kWG) void k_small(Args a, int stage_bytes) {
 
 // Multi-workgroup path, launch 1: selection, per-workgroup histogram row and
 // one record (expert, rank inside the workgroup) per slot.
-template <int EPLM, bool BF16, int MODE>
-__global__ __launch_bounds__(kWG) void k_select(Args a, int stage_bytes) {
-  const Lds L = carve(KIND_SELECT, a, stage_bytes);
+template <int SEG, int EPL, bool BF16, int MODE>
+__global__ __launch_bounds__(kWG) void k_select(Args a) {
+  const Lds L = carve(KIND_SELECT, a);
   const int w = blockIdx.x;
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
-  select_tokens<EPLM, BF16, MODE>(a, L, t0, nt);
+  select_tokens<SEG, EPL, BF16, MODE>(a, L, t0, nt);
   for (int e = threadIdx.x; e < a.E; e += kWG)
     a.ws_hist[(size_t)w * a.E + e] = __popcll(L.bits[e]);
   const int ns = nt * a.k;
@@ -793,54 +965,87 @@ __global__ __launch_bounds__(kWG) void k_select(Args a, int stage_bytes) {
 }
 
 // Launch 2: per expert, exclusive scan of its histogram column in workgroup
-// order (in place) and the padded total.  A block covers 32 experts; each of
-// its 16 row ranges is summed, the sums are scanned across in LDS, and the
-// rows are rewritten as prefixes.
-constexpr int kColE = 32;
+// order (in place) and the padded total.  A block covers 8 experts; each of
+// its 64 row ranges is summed (rows kept in registers when a range has at
+// most 16 rows), the sums are scanned across in LDS, and the rows rewritten.
+constexpr int kColE = 8;
 constexpr int kColParts = kWG / kColE;
+constexpr int kColRegRows = 16;
 
 __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
   __shared__ int part[kColParts][kColE];
   const int ex = threadIdx.x % kColE;
   const int pt = threadIdx.x / kColE;
   const int e = blockIdx.x * kColE + ex;
+  const bool ok = e < a.E;
   const int chunk = (a.nwg + kColParts - 1) / kColParts;
   const int w0 = min(a.nwg, pt * chunk);
   const int w1 = min(a.nwg, w0 + chunk);
+  int32_t* col = a.ws_hist + (ok ? e : 0);
+  const size_t stride = (size_t)a.E;
+  const bool inreg = chunk <= kColRegRows;
+  int v[kColRegRows];
   int s = 0;
-  if (e < a.E) {
+  if (inreg) {
+#pragma unroll
+    for (int r = 0; r < kColRegRows; ++r) {
+      v[r] = (ok && w0 + r < w1) ? col[(size_t)(w0 + r) * stride] : 0;
+      s += v[r];
+    }
+  } else if (ok) {
 #pragma unroll 8
-    for (int w = w0; w < w1; ++w) s += a.ws_hist[(size_t)w * a.E + e];
+    for (int w = w0; w < w1; ++w) s += col[(size_t)w * stride];
   }
   part[pt][ex] = s;
   __syncthreads();
   int pre = 0, total = 0;
   for (int q = 0; q < kColParts; ++q) {
-    if (q < pt) pre += part[q][ex];
-    total += part[q][ex];
+    const int x = part[q][ex];
+    pre += q < pt ? x : 0;
+    total += x;
   }
-  if (e < a.E) {
-    int32_t* col = a.ws_hist + e;
+  if (!ok) return;
+  if (inreg) {
+#pragma unroll
+    for (int r = 0; r < kColRegRows; ++r) {
+      if (w0 + r < w1) {
+        col[(size_t)(w0 + r) * stride] = pre;
+        pre += v[r];
+      }
+    }
+  } else {
 #pragma unroll 8
     for (int w = w0; w < w1; ++w) {
-      const int v = col[(size_t)w * a.E];
-      col[(size_t)w * a.E] = pre;
-      pre += v;
+      const int x = col[(size_t)w * stride];
+      col[(size_t)w * stride] = pre;
+      pre += x;
     }
-    if (pt == 0) {
-      a.ws_tot[e] = total;
-      a.ws_pad[e] = pad_up(total, a.block);
-    }
+  }
+  if (pt == 0) {
+    a.ws_tot[e] = total;
+    a.ws_pad[e] = pad_up(total, a.block);
   }
 }
 
 // Launch 3: expert offsets, padding, expert_of_block and the stable scatter.
+// The slot records are loaded before the offset scan so the two global reads
+// overlap.
+constexpr int kRecPerThread = (kTwMax * 64 + kWG - 1) / kWG;
+
 __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
-  const Lds L = carve(KIND_SCATTER, a, 0);
+  const Lds L = carve(KIND_SCATTER, a);
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
+  const int ns = nt * a.k;
+  const int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
+  int rv[kRecPerThread];
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j) {
+    const int q = tid + j * kWG;
+    rv[j] = q < ns ? rec[q] : 0;
+  }
   const int total = expert_offsets(a, L, [&](int e) { return a.ws_pad[e]; });
   if (w == 0 && tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
@@ -853,13 +1058,14 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
     for (int r = c + tid; r < p; r += kWG) a.sorted_ids[o + r] = sentinel;
     for (int b = tid; b < p / a.block; b += kWG) a.eob[o / a.block + b] = e;
   }
-  const int ns = nt * a.k;
-  const int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
   const int32_t* colpre = a.ws_hist + (size_t)w * a.E;
-  for (int q = tid; q < ns; q += kWG) {
-    const int r = rec[q];
-    const int e = r & 0xFFFF;
-    a.sorted_ids[L.off[e] + colpre[e] + (r >> 16)] = t0 * a.k + q;
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j) {
+    const int q = tid + j * kWG;
+    if (q < ns) {
+      const int e = rv[j] & 0xFFFF;
+      a.sorted_ids[L.off[e] + colpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
+    }
   }
 }
 
@@ -902,32 +1108,47 @@ size_t workspace_of(int M, int E, int k) {
          align16((size_t)M * k * 4);
 }
 
-int eplm_bucket(int epl) {
-  int b = 1;
-  while (b < epl) b <<= 1;
-  return b;
+typedef void (*KernelFn)(Args);
+
+// Experts per lane compiled as constants (straight-line code).  With 64-lane
+// segments any other value runs the variant that reads it at run time; 32-lane
+// segments are used only for the listed values.  A lane run that is a whole
+// number of 16-byte vectors loads straight from HBM (LOAD_VEC), otherwise the
+// rows go through the wave's LDS staging buffers (LOAD_STAGE).
+constexpr bool vec_mode(int epl, bool bf16) { return (epl * (bf16 ? 2 : 4)) % 16 == 0; }
+bool seg32_epl(int epl) {
+  return epl == 2 || epl == 4 || epl == 8 || epl == 16 || epl == 28 || epl == 32;
 }
 
-typedef void (*KernelFn)(Args, int);
-
-#define MRS_PICK(KER)                                                                        \
-  template <bool BF16, int MODE>                                                             \
-  KernelFn pick2_##KER(int eplm) {                                                           \
-    switch (eplm) {                                                                          \
-      case 1: return KER<1, BF16, MODE>;                                                     \
-      case 2: return KER<2, BF16, MODE>;                                                     \
-      case 4: return KER<4, BF16, MODE>;                                                     \
-      case 8: return KER<8, BF16, MODE>;                                                     \
-      case 16: return KER<16, BF16, MODE>;                                                   \
-      case 32: return KER<32, BF16, MODE>;                                                   \
-      default: return KER<64, BF16, MODE>;                                                   \
-    }                                                                                        \
-  }                                                                                          \
-  KernelFn pick_##KER(int eplm, bool bf16, int mode) {                                       \
-    if (bf16) return mode == LOAD_VEC ? pick2_##KER<true, LOAD_VEC>(eplm)                    \
-                                      : pick2_##KER<true, LOAD_STAGE>(eplm);                 \
-    return mode == LOAD_VEC ? pick2_##KER<false, LOAD_VEC>(eplm)                             \
-                            : pick2_##KER<false, LOAD_STAGE>(eplm);                          \
+#define MRS_PICK(KER)                                                                              \
+  template <int SEG, int EPL, bool BF16>                                                           \
+  KernelFn fix_##KER() { return KER<SEG, EPL, BF16, vec_mode(EPL, BF16) ? LOAD_VEC : LOAD_STAGE>; } \
+  template <bool BF16>                                                                             \
+  KernelFn pick1_##KER(int seg, int epl, int mode) {                                               \
+    if (seg == 32) {                                                                               \
+      switch (epl) {                                                                               \
+        case 2: return fix_##KER<32, 2, BF16>();                                                   \
+        case 4: return fix_##KER<32, 4, BF16>();                                                   \
+        case 8: return fix_##KER<32, 8, BF16>();                                                   \
+        case 16: return fix_##KER<32, 16, BF16>();                                                 \
+        case 28: return fix_##KER<32, 28, BF16>();                                                 \
+        case 32: return fix_##KER<32, 32, BF16>();                                                 \
+        default: return nullptr;                                                                   \
+      }                                                                                            \
+    }                                                                                              \
+    switch (epl) {                                                                                 \
+      case 1: return fix_##KER<64, 1, BF16>();                                                     \
+      case 2: return fix_##KER<64, 2, BF16>();                                                     \
+      case 4: return fix_##KER<64, 4, BF16>();                                                     \
+      case 8: return fix_##KER<64, 8, BF16>();                                                     \
+      case 14: return fix_##KER<64, 14, BF16>();                                                   \
+      case 16: return fix_##KER<64, 16, BF16>();                                                   \
+      case 32: return fix_##KER<64, 32, BF16>();                                                   \
+      default: return mode == LOAD_VEC ? KER<64, 0, BF16, LOAD_VEC> : KER<64, 0, BF16, LOAD_STAGE>; \
+    }                                                                                              \
+  }                                                                                                \
+  KernelFn pick_##KER(int seg, int epl, bool bf16, int mode) {                                     \
+    return bf16 ? pick1_##KER<true>(seg, epl, mode) : pick1_##KER<false>(seg, epl, mode);         \
   }
 MRS_PICK(k_small)
 MRS_PICK(k_select)
@@ -1018,9 +1239,6 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   a.block = block;
   a.G = E / n_group;
   a.gstage = (n_group > 1 && topk_group < n_group && a.G > 1) ? 1 : 0;
-  a.fast = (E % kWave == 0 && kWave % n_group == 0 && !(flags & MRS_FLAG_FORCE_EXACT)) ? 1 : 0;
-  a.epl = E / kWave;
-  a.lpg = kWave / n_group;
   a.out_ids = out_ids;
   a.out_w = out_w;
   a.sorted_ids = sorted_ids;
@@ -1029,23 +1247,53 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   a.stats = stats;
   const bool bf16 = logits_dtype == MRS_DTYPE_BF16;
   const int sz = bf16 ? 2 : 4;
-  const int eplm = a.fast ? eplm_bucket(a.epl) : 1;
-  // lane runs that are whole 16-byte vectors load straight from HBM; others
-  // go through a per-wave LDS copy of the row
-  const int mode = (a.fast && (a.epl * sz) % 16 == 0) ? LOAD_VEC : LOAD_STAGE;
-  int stage_bytes = (a.fast && mode == LOAD_STAGE) ? E * sz : 0;
+  const bool want_small = M <= kTwMax && !(flags & MRS_FLAG_FORCE_MULTI_WG);
+  const int tw = want_small ? M : choose_tw(M);
 
-  const bool small_fits = M <= kTwMax &&
-                          lds_plan(KIND_SMALL, E, n_group, a.gstage, a.fast, stage_bytes, M, k).total <= kLdsLimit;
-  const bool small = small_fits && !(flags & MRS_FLAG_FORCE_MULTI_WG);
+  // Wave layout: 32-lane segments (two tokens per wave) when the shape allows
+  // and more than one token per wave is available, else 64-lane segments,
+  // else the workgroup-wide exact path for every token.
+  auto seg_ok = [&](int seg) {
+    return E % seg == 0 && seg % n_group == 0 && E / seg <= 64 && (seg == 64 || seg32_epl(E / seg));
+  };
+  a.fast = 0;
+  a.seg = kWave;
+  if (!(flags & MRS_FLAG_FORCE_EXACT)) {
+    const int order[2] = {tw > kNW ? 32 : 64, tw > kNW ? 64 : 32};
+    for (int q = 0; q < 2 && !a.fast; ++q) {
+      const int seg = order[q];
+      if (!seg_ok(seg)) continue;
+      const int epl = E / seg;
+      const int sb = vec_mode(epl, bf16) ? 0 : E * sz;
+      const int nbuf = tw > kNW * (kWave / seg) ? 2 : 1;
+      const LdsPlan pl = lds_plan(want_small ? KIND_SMALL : KIND_SELECT, E, n_group, a.gstage,
+                                  stage_total(1, seg, nbuf, sb), tw, k);
+      if (pl.total > kLdsLimit) continue;
+      a.fast = 1;
+      a.seg = seg;
+      a.epl = epl;
+      a.stage_bytes = sb;
+      a.nbuf = nbuf;
+    }
+  }
+  if (!a.fast) {
+    a.epl = 1;
+    a.stage_bytes = 0;
+    a.nbuf = 1;
+  }
+  const int mode = a.stage_bytes ? LOAD_STAGE : LOAD_VEC;
+  const size_t stg = stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes);
+
+  const bool small_fits = M <= kTwMax && lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, M, k).total <= kLdsLimit;
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && !small_fits) return MRS_ERR_INVALID_ARG;
-  if (small) {
+  if (want_small && small_fits) {
     a.tw = M;
     a.nwg = 1;
-    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, a.fast, stage_bytes, a.tw, k).total;
-    void* params[] = {&a, &stage_bytes};
-    return launch(reinterpret_cast<const void*>(pick_k_small(eplm, bf16, mode)), 1, lds, st, params);
+    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k).total;
+    void* params[] = {&a};
+    return launch(reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode)), 1, lds, st, params);
   }
+  if (want_small) return MRS_ERR_INVALID_ARG;  // cannot happen: the multi-workgroup plan is no larger
 
   a.tw = choose_tw(M);
   a.nwg = (M + a.tw - 1) / a.tw;
@@ -1059,12 +1307,11 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
-  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, a.fast, stage_bytes, a.tw, k).total;
-  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, a.fast, 0, a.tw, k).total;
+  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, stg, a.tw, k).total;
+  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
-  void* p_sel[] = {&a, &stage_bytes};
   void* p_one[] = {&a};
-  int rc = launch(reinterpret_cast<const void*>(pick_k_select(eplm, bf16, mode)), a.nwg, lds_sel, st, p_sel);
+  int rc = launch(reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode)), a.nwg, lds_sel, st, p_one);
   if (rc == MRS_OK)
     rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, 0, st, p_one);
   if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, lds_sct, st, p_one);

@@ -57,7 +57,7 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr):
     inp = workloads.make_inputs(cfg)
     x0, b = to_gpu(inp, torch)
     mb = x0.numel() * x0.element_size() / 1e6
-    nrot = max(1, int(math.ceil(rotate_mb / mb))) if rotate_mb > 0 else 1
+    nrot = min(64, max(1, int(math.ceil(rotate_mb / mb)))) if rotate_mb > 0 else 1
     # distinct buffers with the same rows in a rotated order: same distribution,
     # no reuse of cached lines between consecutive steps
     xs = [x0] + [torch.roll(x0, shifts=(i * 997) % max(cfg.M, 1), dims=0).contiguous()

@@ -132,6 +132,16 @@ SWEEP = [
     (9, 4095, 3, 3, 1, 3, "bf16", "hot"),
     (90, 768, 6, 96, 10, 24, "f32", "normal"),       # 96 groups of 8
     (12, 17, 1, 1, 1, 1, "f32", "normal"),
+    (70, 4032, 8, 63, 30, 16, "f32", "normal"),        # staged rows too large for LDS
+    (70, 2240, 16, 8, 4, 64, "bf16", "normal"),        # 35 experts per lane, staged
+    # two tokens per wave (32-lane segments)
+    (40, 896, 16, 8, 4, 32, "bf16", "normal"),         # one workgroup, staged rows, two buffers
+    (4500, 128, 8, 4, 2, 8, "f32", "shared"),
+    (5000, 896, 16, 8, 4, 128, "f32", "normal"),
+    (6000, 512, 8, 16, 4, 32, "bf16", "hot"),
+    (8300, 896, 16, 8, 4, 128, "bf16", "log_zipf"),   # staged rows, two buffers
+    (9000, 1024, 8, 32, 8, 64, "bf16", "normal"),     # one lane per group
+    (20000, 64, 4, 2, 1, 16, "f32", "normal"),        # three rounds per wave
 ]
 
 
