@@ -32,6 +32,7 @@ FLAG_FORCE_EXACT = 4
 EXPORTED = [
     "moe_route_sort",
     "moe_route_sort_ex",
+    "moe_route_sort_profiled",
     "moe_route_sort_max_rows",
     "moe_route_sort_max_blocks",
     "moe_route_sort_workspace_bytes",
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort.restype = i32
     L.moe_route_sort_ex.argtypes = common + [ctypes.c_uint, vp]
     L.moe_route_sort_ex.restype = i32
+    L.moe_route_sort_profiled.argtypes = common + [ctypes.c_uint, vp, vp, vp]
+    L.moe_route_sort_profiled.restype = i32
     for name in ("moe_route_sort_max_rows", "moe_route_sort_max_blocks"):
         getattr(L, name).argtypes = [i32, i32, i32, i32]
         getattr(L, name).restype = ctypes.c_int64
@@ -127,7 +130,7 @@ def _workspace(device, nbytes: int):
 
 def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
                out: Optional[RouteSortOutput] = None, workspace=None, flags: int = 0,
-               stats=None, stream=None) -> RouteSortOutput:
+               stats=None, stream=None, events=None) -> RouteSortOutput:
     """Run the route-sort path on the GPU.
 
     logits: [M, E] float32 or bfloat16 CUDA/HIP tensor, contiguous.
@@ -136,6 +139,10 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
     workspace: optional uint8 tensor of at least workspace_bytes() bytes that
             was zeroed once; by default a cached per-device buffer is used.
     stats:  optional int32 [2] device tensor (exact-path / fast-path token counts).
+    events: optional list of 6 torch.cuda.Event(enable_timing=True); events
+            2i and 2i+1 take the start and end of the call's kernel i (pairs
+            past the last kernel are recorded after it); returns
+            (output, launches) then.
     """
     import torch
     if not (isinstance(logits, torch.Tensor) and logits.is_cuda):
@@ -180,10 +187,23 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    rc = raw_call(logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block,
-                  out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
-                  out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt, ws_ptr, ws_len,
-                  stream.cuda_stream, flags, stats.data_ptr() if stats is not None else None)
+    args = (logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block,
+            out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
+            out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt, ws_ptr, ws_len,
+            stream.cuda_stream, flags, stats.data_ptr() if stats is not None else None)
+    if events is not None:
+        if len(events) != 6:
+            raise ValueError("events must hold 6 torch.cuda.Event objects")
+        for ev in events:
+            if not ev.cuda_event:
+                ev.record(stream)  # torch creates the HIP event on its first record
+        handles = (ctypes.c_void_p * 6)(*[ev.cuda_event for ev in events])
+        n = ctypes.c_int(0)
+        rc = int(lib().moe_route_sort_profiled(*args, handles, ctypes.byref(n)))
+        if rc != MRS_OK:
+            raise RouteSortError(rc)
+        return out, n.value
+    rc = int(lib().moe_route_sort_ex(*args))
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return out

@@ -35,6 +35,7 @@
 //   release/acquire across the eight XCDs), far more than a kernel boundary.
 // M <= 64: everything in one workgroup and one launch.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1154,11 +1155,28 @@ MRS_PICK(k_small)
 MRS_PICK(k_select)
 #undef MRS_PICK
 
-int launch(const void* fn, int grid, size_t lds, hipStream_t stream, void** params) {
+// Optional HIP events of one call (diagnostics): launch i is made with
+// hipExtLaunchKernel, which stamps ev[2i] and ev[2i+1] with the start and end
+// of that kernel's own execution.
+constexpr int kMaxLaunches = 3;
+struct Timing {
+  hipEvent_t ev[2 * kMaxLaunches];
+  int n;  // launches so far
+};
+
+int launch(const void* fn, int grid, int block, size_t lds, hipStream_t stream, void** params, Timing* tm) {
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return MRS_ERR_LAUNCH;
-  const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kWG), params, lds, stream);
+  hipError_t err;
+  if (tm) {
+    if (tm->n >= kMaxLaunches) return MRS_ERR_LAUNCH;
+    err = hipExtLaunchKernel(fn, dim3(grid), dim3(block), params, lds, stream, tm->ev[2 * tm->n],
+                             tm->ev[2 * tm->n + 1], 0);
+    ++tm->n;
+  } else {
+    err = hipLaunchKernel(fn, dim3(grid), dim3(block), params, lds, stream);
+  }
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 
@@ -1200,11 +1218,11 @@ size_t moe_route_sort_workspace_bytes(int M, int E, int k, int block) {
   return workspace_of(M, E, k);
 }
 
-int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,
-                      int topk_group, int block, int32_t* out_ids, float* out_w,
-                      int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
-                      int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
-                      unsigned flags, int32_t* stats) {
+static int route_sort_impl(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                           int topk_group, int block, int32_t* out_ids, float* out_w,
+                           int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                           int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                           unsigned flags, int32_t* stats, Timing* tm) {
   const unsigned known = MRS_FLAG_FORCE_SINGLE_WG | MRS_FLAG_FORCE_MULTI_WG | MRS_FLAG_FORCE_EXACT;
   if ((flags & ~known) != 0u) return MRS_ERR_INVALID_ARG;
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && (flags & MRS_FLAG_FORCE_MULTI_WG)) return MRS_ERR_INVALID_ARG;
@@ -1218,9 +1236,7 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M == 0) {
     void* params[] = {&num_post_pad};
-    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(k_zero_npp), dim3(1), dim3(1),
-                                           params, 0, st);
-    return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
+    return launch(reinterpret_cast<const void*>(k_zero_npp), 1, 1, 0, st, params, tm);
   }
   if (!logits || !bias || !out_ids || !out_w || !sorted_ids || !expert_of_block)
     return MRS_ERR_NULL_POINTER;
@@ -1291,7 +1307,8 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
     a.nwg = 1;
     const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k).total;
     void* params[] = {&a};
-    return launch(reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode)), 1, lds, st, params);
+    return launch(reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode)), 1, kWG, lds, st, params,
+                  tm);
   }
   if (want_small) return MRS_ERR_INVALID_ARG;  // cannot happen: the multi-workgroup plan is no larger
 
@@ -1311,10 +1328,42 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   void* p_one[] = {&a};
-  int rc = launch(reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode)), a.nwg, lds_sel, st, p_one);
+  int rc = launch(reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode)), a.nwg, kWG, lds_sel, st,
+                  p_one, tm);
   if (rc == MRS_OK)
-    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, 0, st, p_one);
-  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, lds_sct, st, p_one);
+    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, kWG, 0, st, p_one, tm);
+  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, tm);
+  return rc;
+}
+
+int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                      int topk_group, int block, int32_t* out_ids, float* out_w,
+                      int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                      int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      unsigned flags, int32_t* stats) {
+  return route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
+                         expert_of_block, num_post_pad, logits_dtype, workspace, workspace_bytes, stream, flags,
+                         stats, nullptr);
+}
+
+int moe_route_sort_profiled(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                            int topk_group, int block, int32_t* out_ids, float* out_w,
+                            int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                            int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                            unsigned flags, int32_t* stats, void* const* events, int* n_launches) {
+  if (!events || !n_launches) return MRS_ERR_NULL_POINTER;
+  Timing tm{};
+  for (int i = 0; i < 2 * kMaxLaunches; ++i) {
+    if (!events[i]) return MRS_ERR_NULL_POINTER;
+    tm.ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  }
+  const int rc = route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
+                                 expert_of_block, num_post_pad, logits_dtype, workspace, workspace_bytes, stream,
+                                 flags, stats, &tm);
+  *n_launches = tm.n;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 2 * tm.n; rc == MRS_OK && i < 2 * kMaxLaunches; ++i)
+    if (hipEventRecord(tm.ev[i], st) != hipSuccess) return MRS_ERR_LAUNCH;
   return rc;
 }
 

@@ -19,6 +19,7 @@ os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
 os.environ.setdefault("MKL_NUM_THREADS", "1")
 
 import argparse  # noqa: E402
+import hashlib  # noqa: E402
 import json  # noqa: E402
 import math  # noqa: E402
 import platform  # noqa: E402
@@ -41,8 +42,25 @@ def log(*a):
 
 
 def algorithmic_bytes(cfg, npp):
+    """Bytes the method must move per call: logits in, bias in, ids + weights
+    out, sorted rows, expert per block and the row count out."""
     sz = 2 if cfg.dtype == "bf16" else 4
     return (cfg.M * cfg.E * sz + 4 * cfg.E + 8 * cfg.M * cfg.k + 4 * npp + 4 * (npp // cfg.block) + 4)
+
+
+def launch_bytes(cfg, npp, launches):
+    """Algorithmic bytes attributed to each launch of one call.  One launch:
+    everything.  Three launches: selection (logits + bias in, ids + weights
+    out), column scan of the workgroup histograms (workspace only), scatter
+    (sorted rows, expert per block, row count)."""
+    if launches == 1:
+        return [algorithmic_bytes(cfg, npp)]
+    sz = 2 if cfg.dtype == "bf16" else 4
+    return [cfg.M * cfg.E * sz + 4 * cfg.E + 8 * cfg.M * cfg.k, 0,
+            4 * npp + 4 * (npp // cfg.block) + 4]
+
+
+KERNELS = {1: ["k_small"], 3: ["k_select", "k_colscan", "k_scatter"]}
 
 
 def to_gpu(inp, torch):
@@ -53,7 +71,7 @@ def to_gpu(inp, torch):
     return x, torch.from_numpy(inp.bias).cuda()
 
 
-def time_workload(cfg, steps, warmup, rotate_mb, torch, amr):
+def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     inp = workloads.make_inputs(cfg)
     x0, b = to_gpu(inp, torch)
     mb = x0.numel() * x0.element_size() / 1e6
@@ -83,27 +101,59 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr):
         torch.cuda.synchronize()
     wall_us = (time.perf_counter() - t) / reps * 1e6
     nbytes = algorithmic_bytes(cfg, npp)
-    return dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
-                routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9)
+    r = dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
+             routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9)
+    if per_kernel:
+        # HIP events stamped with each kernel's own start and end by the
+        # library's launches (hipExtLaunchKernel), same rotation of inputs
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        launches = 0
+        for i in range(steps):
+            _, launches = amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
+                                         out=out, events=evs[i])
+        torch.cuda.synchronize()
+        per = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(launches)]
+                        for i in range(steps)]) * 1e3  # us
+        r["kernels"] = [dict(name=KERNELS.get(launches, ["?"] * launches)[j], avg_us=float(per[:, j].mean()),
+                             algorithmic_bytes=launch_bytes(cfg, npp, launches)[j])
+                        for j in range(launches)]
+    return r
+
+
+def traffic_record(kernel, workload):
+    """HBM traffic per launch measured with rocprofv3 PMC counters and stored
+    under profiles/, used only while the kernel source still has the hash the
+    counters were taken with."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    src = os.path.join(ROOT, "align_moe_route_amd", "csrc", "moe_route_sort.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != h:
+        return None
+    return rec
 
 
 def cpu_baseline(cfg, budget_s=12.0, chunk=1024):
-    """The oracle as it stands, on the first tokens of the same workload, one
-    oracle call per chunk of tokens, until the time budget is spent."""
+    """The oracle as it stands, on the same workload: one oracle call per chunk
+    of tokens, cycling through the workload's tokens until the time budget is
+    spent (so the sample is about budget_s of single-core work)."""
     from oracle import route_sort as orc
     inp = workloads.make_inputs(cfg)
-    done, spent = 0, 0.0
-    while done < cfg.M and spent < budget_s:
-        rows = np.arange(done, min(cfg.M, done + chunk))
+    done, spent, t0 = 0, 0.0, 0
+    while spent < budget_s:
+        rows = np.arange(t0, min(cfg.M, t0 + chunk))
         t = time.perf_counter()
         orc.route_sort(inp.logits_storage, cfg.dtype, inp.bias, cfg.k, cfg.n_group,
                        cfg.topk_group, cfg.block, tokens=rows)
         spent += time.perf_counter() - t
         done += rows.size
+        t0 = 0 if t0 + chunk >= cfg.M else t0 + chunk
     return dict(value=done * cfg.k / spent, unit="routes/s", cores=1, kind="oracle",
-                sample=f"first {done} of {cfg.M} tokens of {cfg.name} (oracle route_sort per "
-                       f"{chunk}-token chunk: selection + sort metadata), {spent:.1f} s on one "
-                       f"core of {platform.processor() or platform.machine()}")
+                sample=f"{done} tokens of {cfg.name} (its {cfg.M} tokens cycled; oracle route_sort per "
+                       f"{chunk}-token chunk: selection + sort metadata), {spent:.1f} s on one core of "
+                       f"{platform.processor() or platform.machine()}")
 
 
 def main():
@@ -115,6 +165,9 @@ def main():
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--calib-copy-mb", type=float, default=0.0,
+                    help="first run a plain device-to-device copy of this many MB three times "
+                         "(reference dispatches for scaling PMC byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -127,12 +180,27 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     amr.lib()
 
+    if args.calib_copy_mb > 0:
+        n = int(args.calib_copy_mb * 1e6) // 4
+        src = torch.arange(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {4 * n} bytes read and written")
+        del src, dst
+
     cfg = workloads.CONFIGS[args.workload]
     log(f"[bench] {cfg.name}: M={cfg.M} E={cfg.E} k={cfg.k} steps={args.steps} warmup={args.warmup}")
     torch.cuda.synchronize()
-    r = time_workload(cfg, args.steps, args.warmup, args.rotate_mb, torch, amr)
+    r = time_workload(cfg, args.steps, args.warmup, args.rotate_mb, torch, amr, per_kernel=True)
     log(f"[bench] {cfg.name}: {r['ms']*1e3:.2f} us/call, {r['routes_per_s']:.3e} routes/s, "
         f"{r['gbps']:.1f} GB/s algorithmic, {r['rot']} rotating input copies")
+    for kr in r["kernels"]:
+        log(f"[bench]   {kr['name']}: {kr['avg_us']:.2f} us/launch, {kr['algorithmic_bytes']} algorithmic bytes")
+    dom = max(r["kernels"], key=lambda kr: kr["avg_us"])
+    dom_gbps = dom["algorithmic_bytes"] / (dom["avg_us"] * 1e-6) / 1e9
+    tr = traffic_record(dom["name"], cfg.name)
 
     extra = {}
     if not args.no_extra:
@@ -172,9 +240,14 @@ def main():
         "hbm_gbps_algorithmic": r["gbps"],
         "us_per_call": r["ms"] * 1e3,
         "decode_us_per_call": extra.get("decode", {}).get("us_per_call"),
-        "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
-                     "algorithmic_bytes_per_call": r["nbytes"], "scope": "whole call"},
+        "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None,
+                     "algorithmic_bytes_per_launch": dom["algorithmic_bytes"],
+                     "avg_launch_us": dom["avg_us"]},
+        "kernels": r["kernels"],
+        "whole_call": {"algorithmic_bytes": r["nbytes"], "achieved_gbps": r["gbps"],
+                       "frac": r["gbps"] / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
         "other_workloads": extra,
     }

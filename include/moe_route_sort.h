@@ -116,6 +116,24 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
                       int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
                       unsigned flags, int32_t* stats);
 
+/*
+ * moe_route_sort_profiled -- moe_route_sort_ex that also stamps HIP events so
+ * a caller can time the call's kernels one by one (diagnostics for benchmarks;
+ * every kernel does all of its work).  `events` points to 6 hipEvent_t handles
+ * (cast to void*) created by the caller; launch i (i = 0, 1, 2) is made with
+ * hipExtLaunchKernel and stamps events[2i] and events[2i+1] with the start and
+ * the end of that kernel's execution.  Pairs past the last launch are recorded
+ * on `stream` after it (zero elapsed time).  *n_launches receives the number
+ * of kernels launched (1 to 3).  Returns like moe_route_sort_ex;
+ * MRS_ERR_NULL_POINTER when `events`, one of its handles or `n_launches` is
+ * NULL.
+ */
+int moe_route_sort_profiled(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                            int topk_group, int block, int32_t* out_ids, float* out_w,
+                            int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                            int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                            unsigned flags, int32_t* stats, void* const* events, int* n_launches);
+
 /* Capacity of sorted_ids: M*k + min(E, M*k)*(block-1), or -1 when the
  * arguments are invalid or the result does not fit int32. */
 int64_t moe_route_sort_max_rows(int M, int E, int k, int block);

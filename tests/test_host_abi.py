@@ -116,3 +116,20 @@ def test_sigmoid_probe_validation():
     assert L.moe_route_sort_sigmoid_probe(P, 0, P, P, None) == amr.MRS_OK
     assert L.moe_route_sort_sigmoid_probe(None, 5, P, P, None) == amr.MRS_ERR_NULL_POINTER
     assert L.moe_route_sort_sigmoid_probe(P + 2, 5, P, P, None) == amr.MRS_ERR_MISALIGNED
+
+
+def test_profiled_entry_validation():
+    """The profiled entry point checks its event array before anything else and
+    passes every other check through unchanged (no event is touched on error)."""
+    L = amr.lib()
+    ev = (ctypes.c_void_p * 6)(P, P, P, P, P, P)
+    n = ctypes.c_int(-1)
+    args = [P, P, 4, 64, 4, 8, 4, 16, P, P, P, P, P, amr.MRS_DTYPE_F32, None, 0, None, 0, None]
+    assert L.moe_route_sort_profiled(*args, None, ctypes.byref(n)) == amr.MRS_ERR_NULL_POINTER
+    assert L.moe_route_sort_profiled(*args, ev, None) == amr.MRS_ERR_NULL_POINTER
+    holes = (ctypes.c_void_p * 6)(P, P, P, None, P, P)
+    assert L.moe_route_sort_profiled(*args, holes, ctypes.byref(n)) == amr.MRS_ERR_NULL_POINTER
+    bad = list(args)
+    bad[3] = 0  # E = 0
+    assert L.moe_route_sort_profiled(*bad, ev, ctypes.byref(n)) == amr.MRS_ERR_INVALID_ARG
+    assert n.value == 0
