@@ -38,6 +38,7 @@ EXPORTED = [
     "moe_route_sort_workspace_bytes",
     "moe_route_sort_strerror",
     "moe_route_sort_sigmoid_probe",
+    "moe_route_sort_sigmoid_table_probe",
 ]
 
 _lib = None
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_strerror.restype = ctypes.c_char_p
     L.moe_route_sort_sigmoid_probe.argtypes = [vp, i32, vp, vp, vp]
     L.moe_route_sort_sigmoid_probe.restype = i32
+    L.moe_route_sort_sigmoid_table_probe.argtypes = [vp, i32, vp, vp, vp]
+    L.moe_route_sort_sigmoid_table_probe.restype = i32
     _lib = L
     return L
 
@@ -220,3 +223,17 @@ def sigmoid_probe(x):
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return f, e
+
+
+def sigmoid_table_probe(bits):
+    """Sigmoid of BF16 bit patterns (an int16/uint16-valued GPU tensor) through
+    the kernels' LDS table: (single-value form, packed-pair form)."""
+    import torch
+    h = bits.contiguous().to(torch.int16)
+    o1 = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+    o2 = torch.empty_like(o1)
+    rc = lib().moe_route_sort_sigmoid_table_probe(h.data_ptr(), h.numel(), o1.data_ptr(), o2.data_ptr(),
+                                                  torch.cuda.current_stream(h.device).cuda_stream)
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return o1, o2

@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_route_sort.h"
@@ -47,11 +49,18 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kNW = 8;                   // waves per workgroup
+constexpr int kNW = 16;                  // waves per workgroup
 constexpr int kWG = kNW * kWave;         // threads per workgroup, all kernels
 constexpr int kTwMax = 64;               // tokens per workgroup: one bit each in a 64-bit word
 constexpr int kEMax = 4096;              // 16 KiB of 32-bit counters, the pages' LDS bound
-constexpr int kBiasRegMax = 16;          // lanes keep their biases in registers up to this many experts
+constexpr int kBiasRegMax = 32;          // lanes keep their biases in registers up to this many experts
+// Correctly rounded sigmoid of every BF16 value, 8192 FP32 entries: entry
+// 2t + s is the value at the BF16 pattern (0x3300 + t) | s << 15.  Below the
+// window (|x| < 2^-25) the sigmoid rounds to 0.5, above it (|x| >= 128) to 1
+// or 0, so clamping t into [0, 4095] gives the exact value for every BF16 x.
+constexpr int kSigEntries = 8192;
+constexpr int kSigBytes = kSigEntries * 4;
+constexpr uint32_t kSigBase = 0x3300;
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kWsHeader = 256;
 
@@ -71,6 +80,8 @@ struct Args {
   int tw;      // tokens per workgroup
   int nwg;     // workgroups of the multi-workgroup path
   int fast;    // the wave layout covers this shape
+  int tbl;     // BF16 logits: keys from the sigmoid table in LDS (exact)
+  int bias_dma;  // bias is copied into LDS by DMA (16-byte aligned, E % 4 == 0)
   int gstage;  // the group stage changes the result (1 < topk_group < n_group, G > 1)
   int32_t* out_ids;
   float* out_w;
@@ -88,7 +99,7 @@ struct Args {
 // LDS plan shared by host (size) and device (carving).
 // ----------------------------------------------------------------------------
 struct LdsPlan {
-  size_t bits, redd, off, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
+  size_t sig, bits, redd, off, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
 __host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes) {
@@ -96,10 +107,11 @@ __host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int s
 }
 
 __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gstage, size_t stage,
-                                            int tw, int k) {
+                                            int tw, int k, int tbl) {
   LdsPlan p{};
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
+  if (kind != KIND_SCATTER && tbl) p.sig = take(kSigBytes);  // at LDS offset 0
   if (kind != KIND_SCATTER) p.bits = take((size_t)E * 8);
   p.redd = take((size_t)kNW * 8);
   if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
@@ -108,7 +120,7 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
     p.bias = take((size_t)E * 4);
     p.cand_i = take((size_t)kNW * kWave * 4);
     p.cand_c = take((size_t)kNW * kWave * 8);
-    p.gcomp = take((size_t)kNW * kWave * 8);
+    p.gcomp = p.cand_c;  // group composites (step 2) and candidate keys (step 5) of a wave never overlap
     if (o < 1024) o = 1024;  // staging buffers start past 1 KiB (see stage_rows_async)
     // union: wave staging buffers (wave loop) / exact keys + group arrays (after it)
     const size_t ex = (size_t)E * 4 + (gstage ? (size_t)3 * n_group * 4 + 16 : 0);
@@ -148,7 +160,7 @@ extern __shared__ __align__(16) unsigned char g_lds[];
 
 __device__ inline Lds carve(int kind, const Args& a) {
   const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes),
-                             a.tw, a.k);
+                             a.tw, a.k, a.tbl);
   Lds L;
   L.bits = reinterpret_cast<unsigned long long*>(g_lds + p.bits);
   L.redd = reinterpret_cast<double*>(g_lds + p.redd);
@@ -239,6 +251,30 @@ __device__ __forceinline__ float sigmoid_exact(float x) {
   const double e = exp(-xd);
   return (float)(1.0 / (1.0 + e));
 }
+
+// The sigmoid table (built once per device by k_build_sig_table from
+// sigmoid_exact, copied into LDS offset 0 by every workgroup that uses it).
+__device__ __align__(16) float g_sig_table[kSigEntries];
+
+// Byte offset of a BF16 pattern's entry: 8 * clamp(|h| - base, 0, 4095) + 4 * sign.
+__device__ __forceinline__ uint32_t sig_off1(uint32_t h) {
+  const int t = (int)(h & 0x7FFFu) - (int)kSigBase;
+  const uint32_t c = (uint32_t)min(max(t, 0), 4095);
+  return (c << 3) | ((h >> 13) & 4u);
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// Both entries of a pair of BF16 patterns packed in one word (low half first),
+// with packed 16-bit integer arithmetic.
+__device__ __forceinline__ void sig_off2(uint32_t d, uint32_t& o0, uint32_t& o1) {
+  u16x2 m = __builtin_bit_cast(u16x2, d & 0x7FFF7FFFu);
+  m = __builtin_elementwise_sub_sat(m, (u16x2){(unsigned short)kSigBase, (unsigned short)kSigBase});
+  m = __builtin_elementwise_min(m, (u16x2){4095, 4095});
+  m = m << (u16x2){3, 3};
+  const uint32_t v = __builtin_bit_cast(uint32_t, m) | ((d >> 13) & 0x00040004u);
+  o0 = v & 0xFFFFu;
+  o1 = v >> 16;
+}
+__device__ __forceinline__ float sig_lds(uint32_t off) { return *reinterpret_cast<const float*>(g_lds + off); }
 
 // ----------------------------------------------------------------------------
 // Wave-level helpers (wave64, DPP row shifts and broadcasts).
@@ -599,10 +635,16 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
   return (bal >> (s * SEG)) & 0xFFFFFFFFull;
 }
 
+// One token per segment.  BF16 logits take their correctly rounded sigmoid
+// from the LDS table, so every key is exact from the start and the token is
+// decided in one pass.  FP32 logits rank with sigmoid_fast and a certified
+// margin (see the header comment); `exact` = the redo pass with correctly
+// rounded keys.
 template <int SEG, int EPL, bool BF16, int MODE>
 __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, int t, int tl,
                                          const unsigned char* stage, const float* bv, double delta,
                                          double epsg, bool exact) {
+  constexpr bool TBL = BF16;
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
   using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
@@ -616,27 +658,43 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   constexpr int SZ = BF16 ? 2 : 4;
   const unsigned long long below = (SEG == 64) ? ((1ull << lane) - 1ull) : ((1ull << ls) - 1ull);
   int status = act ? TOK_DONE : TOK_ESCALATE;  // an idle segment writes nothing
+  if (TBL) exact = true;
 
   // ---- 1. keys and lane top-2 ----
   float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
   auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.bias[e0 + i]; };
-  auto put = [&](int i, float x) {
-    const float key = (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i);
+  auto put_key = [&](int i, float key) {
     av[i] = key;
-    l2 = fmaxf(l2, fminf(lm, key));
+    l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
     lm = fmaxf(lm, key);
+  };
+  auto put = [&](int i, float x) {  // FP32 logits
+    put_key(i, (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i));
     if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
+  };
+  auto put_pair = [&](int i, uint32_t d) {  // BF16 logits of experts i, i+1 packed in d
+    uint32_t o0, o1;
+    sig_off2(d, o0, o1);
+    put_key(i, sig_lds(o0) + bias_of(i));
+    put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
   };
 #pragma unroll
   for (int i = 0; i < EPLM; ++i) av[i] = -INFINITY;
   if (act) {
     if constexpr (MODE == LOAD_STAGE) {  // the row is already in this segment's LDS buffer
       if constexpr (BF16) {
-        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
+        if (EPL > 0 ? (EPL % 2 == 0) : (epl % 2 == 0)) {  // the lane run is 4-byte aligned
+          const uint32_t* s32 = reinterpret_cast<const uint32_t*>(stage + e0 * 2);
 #pragma unroll
-        for (int i = 0; i < EPLM; ++i)
-          if (i < epl) put(i, __uint_as_float((uint32_t)s16[i] << 16));
+          for (int j = 0; j < EPLM / 2; ++j)
+            if (2 * j < epl) put_pair(2 * j, s32[j]);
+        } else {
+          const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
+#pragma unroll
+          for (int i = 0; i < EPLM; ++i)
+            if (i < epl) put_key(i, sig_lds(sig_off1(s16[i])) + bias_of(i));
+        }
       } else {
         const float* s32 = reinterpret_cast<const float*>(stage) + e0;
 #pragma unroll
@@ -655,12 +713,8 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
           const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            if constexpr (BF16) {
-              put(q * PER + 2 * j, __uint_as_float(d[j] << 16));
-              put(q * PER + 2 * j + 1, __uint_as_float(d[j] & 0xFFFF0000u));
-            } else {
-              put(q * PER + j, __uint_as_float(d[j]));
-            }
+            if constexpr (BF16) put_pair(q * PER + 2 * j, d[j]);
+            else put(q * PER + j, __uint_as_float(d[j]));
           }
         }
       }
@@ -697,10 +751,12 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
       if (act && !(gap > 2.0 * epsg)) status = TOK_REDO_EXACT;
     }
     allowed = act && keep;
+    wave_sync_lds();  // every lane has read the composites before step 5 reuses the space
   }
 
   // ---- 3. threshold: k-th largest of the kept lanes' two largest keys ----
-  // (at least k keys reach it, so every exact top-k key has A >= it - 2 delta)
+  // (at least k keys reach it: the exact top-k keys are all >= it with exact
+  // keys, >= it - 2 delta with fast keys)
   constexpr int R = EPLM >= 2 ? 2 : 1;
   const int nallow = (int)__popcll(seg_bits<SEG>(__ballot(allowed), seg));
   if (status == TOK_DONE && nallow * (EPL == 1 || (EPL == 0 && epl < 2) ? 1 : R) < a.k) status = TOK_ESCALATE;
@@ -717,7 +773,7 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
     tops[s] = (hi == lo || lo > hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
     Ts[s] = tops[s] < 0 ? min(hi, lo) : (hi & ~((2u << tops[s]) - 1u));  // every value counted is >= Ts
   }
-  constexpr int kSteps = 12;  // resolve the 12 highest differing bits
+  constexpr int kSteps = 10;  // resolve the 10 highest differing bits
   for (int j = 0; j < kSteps; ++j) {
     uint32_t cs[NSEG];
 #pragma unroll
@@ -742,8 +798,7 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   // ---- 4. candidates, compacted in expert order ----
   MaskT cm = 0;
 #pragma unroll
-  for (int i = 0; i < EPLM; ++i)
-    if (i < epl && av[i] >= thr) cm |= (MaskT)1 << i;
+  for (int i = EPLM - 1; i >= 0; --i) cm = cm + cm + ((i < epl && av[i] >= thr) ? 1 : 0);  // bit i = expert i
   if (!allowed || status != TOK_DONE) cm = 0;
   const int mine = (int)__popcll((unsigned long long)cm);
   const int incl = seg_incl_scan<SEG>(mine);
@@ -763,18 +818,20 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   // ---- 5. exact keys of the candidates, ranks by (key desc, index asc) ----
   const bool has = status == TOK_DONE && ls < total;
   const int ce = has ? ci[ls] : 0;
-  double s = 0.0;
+  float sf = 0.0f;
   unsigned long long mykey = 0ull;  // below every real key
   if (has) {
-    float x;
-    if constexpr (MODE == LOAD_STAGE) {
-      if constexpr (BF16) x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(stage)[ce] << 16);
-      else x = reinterpret_cast<const float*>(stage)[ce];
+    if constexpr (TBL) {
+      uint32_t h;
+      if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
+      else h = reinterpret_cast<const uint16_t*>(a.logits)[row + ce];
+      sf = sig_lds(sig_off1(h));
     } else {
-      x = load_logit<BF16>(a.logits, row + ce);
+      float x;
+      if constexpr (MODE == LOAD_STAGE) x = reinterpret_cast<const float*>(stage)[ce];
+      else x = load_logit<BF16>(a.logits, row + ce);
+      sf = sigmoid_exact(x);
     }
-    const float sf = sigmoid_exact(x);
-    s = (double)sf;
     mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
   }
   unsigned long long* cc = L.cand_c + w * kWave + seg * SEG;
@@ -790,12 +847,12 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   }
   const bool sel = has && rank < a.k;
 
-  // ---- 6. outputs in expert order, weights in float64 ----
+  // ---- 6. outputs in expert order; weights s / sum(s), the sum in float64 ----
   const int pos = (int)__popcll(seg_bits<SEG>(__ballot(sel), seg) & below);
-  const double ssum = seg_sum_d<SEG>(sel ? s : 0.0);
+  const double ssum = seg_sum_d<SEG>(sel ? (double)sf : 0.0);
   if (sel) {
     a.out_ids[(size_t)t * a.k + pos] = ce;
-    a.out_w[(size_t)t * a.k + pos] = (float)(s / ssum);
+    a.out_w[(size_t)t * a.k + pos] = (float)((double)sf / ssum);
     atomicOr(&L.bits[ce], 1ull << tl);
     L.ids[tl * a.k + pos] = ce;
   }
@@ -821,11 +878,31 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     const int tl = tok_of(0);
     stage_rows_async<SEG>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
   }
+  // sigmoid table and bias into LDS by DMA, in flight together with the rows
+  const int wbase = w * kWave * 16;  // LDS bytes of the lanes before this wave in one pass
+  if (a.tbl) {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(g_sig_table);
+    for (int j = 0; j * kWG * 16 < kSigBytes; ++j)
+      __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
+                                       (__attribute__((address_space(3))) void*)(g_lds + j * kWG * 16 + wbase), 16,
+                                       0, 0);
+  }
+  if (a.bias_dma) {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.bias);
+    unsigned char* dst = reinterpret_cast<unsigned char*>(L.bias);
+    const int chunks = a.E / 4;
+    for (int j = 0; j * kWG < chunks; ++j)
+      if (j * kWG + tid < chunks)
+        __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + j * kWG * 16 + wbase), 16,
+                                         0, 0);
+  }
   for (int e = tid; e < a.E; e += kWG) {
     L.bits[e] = 0ull;
-    L.bias[e] = a.bias[e];
+    if (!a.bias_dma) L.bias[e] = a.bias[e];
   }
   if (tid == 0) L.misc[0] = 0;
+  if (a.tbl || a.bias_dma) wait_vmem_all();  // this wave's DMA has landed (rows included)
   __syncthreads();
   if (a.fast) {
     const int epl = EPL > 0 ? EPL : a.epl;
@@ -1080,11 +1157,38 @@ __global__ __launch_bounds__(256) void k_sigmoid_probe(const float* x, int n, fl
   }
 }
 
+// Entry 2t + s of the table = correctly rounded sigmoid at BF16 pattern
+// (kSigBase + t) | s << 15.
+__global__ __launch_bounds__(256) void k_build_sig_table() {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < kSigEntries) {
+    const uint32_t h = ((kSigBase + (uint32_t)(j >> 1)) & 0x7FFFu) | ((uint32_t)(j & 1) << 15);
+    g_sig_table[j] = sigmoid_exact(__uint_as_float(h << 16));
+  }
+}
+
+// Sigmoid of BF16 patterns through the LDS table, by the single-value (o1)
+// and the packed-pair (o2, pairing element i with i ^ 1) address forms.
+__global__ __launch_bounds__(256) void k_sigmoid_table_probe(const uint16_t* h, int n, float* o1, float* o2) {
+  float* tab = reinterpret_cast<float*>(g_lds);
+  for (int j = threadIdx.x; j < kSigEntries; j += 256) tab[j] = g_sig_table[j];
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    o1[i] = sig_lds(sig_off1(h[i]));
+    const int p = i & ~1;
+    const uint32_t d = (uint32_t)h[p] | ((p + 1 < n ? (uint32_t)h[p + 1] : 0u) << 16);
+    uint32_t a0, a1;
+    sig_off2(d, a0, a1);
+    o2[i] = sig_lds((i & 1) ? a1 : a0);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
 int choose_tw(int M) {
-  int tw = (M + 511) / 512;
+  int tw = (M + 255) / 256;  // one workgroup per compute unit
   if (tw < 1) tw = 1;
   if (tw > kTwMax) tw = kTwMax;
   return tw;
@@ -1181,6 +1285,33 @@ int launch(const void* fn, int grid, int block, size_t lds, hipStream_t stream, 
 }
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// The sigmoid table is built once per device, on the first call that needs it:
+// launched on the caller's stream and waited for (the only host wait of the
+// library).  A first call made under stream capture puts the build into the
+// captured graph instead and leaves the device marked as not built.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_table_ready[kMaxDevices];
+std::mutex g_table_mu;
+
+int ensure_sig_table(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRS_ERR_LAUNCH;
+  if (g_table_ready[dev].load(std::memory_order_acquire)) return MRS_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return MRS_ERR_LAUNCH;
+  const void* fn = reinterpret_cast<const void*>(k_build_sig_table);
+  if (cs != hipStreamCaptureStatusNone)
+    return hipLaunchKernel(fn, dim3(kSigEntries / 256), dim3(256), nullptr, 0, st) == hipSuccess ? MRS_OK
+                                                                                          : MRS_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_table_mu);
+  if (g_table_ready[dev].load(std::memory_order_acquire)) return MRS_OK;
+  if (hipLaunchKernel(fn, dim3(kSigEntries / 256), dim3(256), nullptr, 0, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MRS_ERR_LAUNCH;
+  g_table_ready[dev].store(1, std::memory_order_release);
+  return MRS_OK;
+}
 
 }  // namespace
 
@@ -1283,7 +1414,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
       const int sb = vec_mode(epl, bf16) ? 0 : E * sz;
       const int nbuf = tw > kNW * (kWave / seg) ? 2 : 1;
       const LdsPlan pl = lds_plan(want_small ? KIND_SMALL : KIND_SELECT, E, n_group, a.gstage,
-                                  stage_total(1, seg, nbuf, sb), tw, k);
+                                  stage_total(1, seg, nbuf, sb), tw, k, bf16 ? 1 : 0);
       if (pl.total > kLdsLimit) continue;
       a.fast = 1;
       a.seg = seg;
@@ -1297,21 +1428,27 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.stage_bytes = 0;
     a.nbuf = 1;
   }
+  a.tbl = (a.fast && bf16) ? 1 : 0;
+  a.bias_dma = (aligned(bias, 16) && E % 4 == 0) ? 1 : 0;
   const int mode = a.stage_bytes ? LOAD_STAGE : LOAD_VEC;
   const size_t stg = stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes);
 
-  const bool small_fits = M <= kTwMax && lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, M, k).total <= kLdsLimit;
+  const bool small_fits =
+      M <= kTwMax && lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, M, k, a.tbl).total <= kLdsLimit;
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && !small_fits) return MRS_ERR_INVALID_ARG;
-  if (want_small && small_fits) {
+  if (want_small && !small_fits) return MRS_ERR_INVALID_ARG;  // cannot happen: the plan above fits
+  if (a.tbl) {
+    const int rc = ensure_sig_table(st);
+    if (rc != MRS_OK) return rc;
+  }
+  if (want_small) {
     a.tw = M;
     a.nwg = 1;
-    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k).total;
+    const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
     void* params[] = {&a};
     return launch(reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode)), 1, kWG, lds, st, params,
                   tm);
   }
-  if (want_small) return MRS_ERR_INVALID_ARG;  // cannot happen: the multi-workgroup plan is no larger
-
   a.tw = choose_tw(M);
   a.nwg = (M + a.tw - 1) / a.tw;
   const size_t need = workspace_of(M, E, k);
@@ -1324,8 +1461,8 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
-  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, stg, a.tw, k).total;
-  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k).total;
+  const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
+  const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k, 0).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   void* p_one[] = {&a};
   int rc = launch(reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode)), a.nwg, kWG, lds_sel, st,
@@ -1374,6 +1511,21 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
   return moe_route_sort_ex(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
                            sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
                            workspace_bytes, stream, 0u, nullptr);
+}
+
+int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* out_single,
+                                       float* out_pair, void* stream) {
+  if (n < 0) return MRS_ERR_INVALID_ARG;
+  if (n == 0) return MRS_OK;
+  if (!bf16_bits || !out_single || !out_pair) return MRS_ERR_NULL_POINTER;
+  if (!aligned(bf16_bits, 2) || !aligned(out_single, 4) || !aligned(out_pair, 4)) return MRS_ERR_MISALIGNED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rc = ensure_sig_table(st);
+  if (rc != MRS_OK) return rc;
+  void* params[] = {&bf16_bits, &n, &out_single, &out_pair};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_table_probe), dim3((n + 255) / 256),
+                                         dim3(256), params, kSigBytes, st);
+  return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 
 int moe_route_sort_sigmoid_probe(const float* x, int n, float* fast_out, float* exact_out,

@@ -261,6 +261,21 @@ def test_exact_sigmoid_bit_exact_on_all_bf16():
     assert err.max() < 2.0 ** -22
 
 
+def test_sigmoid_table_bit_exact_on_all_bf16():
+    """The LDS table that BF16 logits are scored with, through both address
+    forms, equals the oracle's correctly rounded sigmoid on every finite BF16
+    value (including zeros, subnormals and both clamped ends)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = orc.bf16_bits_to_f32(bits)
+    fin = np.isfinite(x)
+    o1, o2 = amr.sigmoid_table_probe(torch.from_numpy(bits.view(np.int16)).cuda())
+    ref = orc.sigmoid_f32(x[fin])
+    for o in (o1, o2):
+        got = o.cpu().numpy()[fin]
+        bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, (x[fin][bad[:8]], got[bad[:8]], ref[bad[:8]])
+
+
 def test_sigmoid_forms_on_fp32_grid():
     rng = np.random.default_rng(4)
     x = np.concatenate([np.linspace(-110, 40, 400001), rng.standard_normal(200000) * 3,

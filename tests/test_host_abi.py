@@ -133,3 +133,11 @@ def test_profiled_entry_validation():
     bad[3] = 0  # E = 0
     assert L.moe_route_sort_profiled(*bad, ev, ctypes.byref(n)) == amr.MRS_ERR_INVALID_ARG
     assert n.value == 0
+
+
+def test_sigmoid_table_probe_validation():
+    L = amr.lib()
+    assert L.moe_route_sort_sigmoid_table_probe(P, -1, P, P, None) == amr.MRS_ERR_INVALID_ARG
+    assert L.moe_route_sort_sigmoid_table_probe(P, 0, P, P, None) == amr.MRS_OK
+    assert L.moe_route_sort_sigmoid_table_probe(None, 5, P, P, None) == amr.MRS_ERR_NULL_POINTER
+    assert L.moe_route_sort_sigmoid_table_probe(P + 1, 5, P, P, None) == amr.MRS_ERR_MISALIGNED
