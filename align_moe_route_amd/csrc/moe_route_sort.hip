@@ -42,6 +42,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <unordered_map>
 #include <type_traits>
 
 #include "moe_route_sort.h"
@@ -74,6 +75,7 @@ struct Args {
   int M, E, k, n_group, topk_group, block;
   int G;       // experts per group
   int seg;    // lanes per token in the wave path (32 or 64)
+  int lg_lpg;  // log2 of the lanes per group in the wave path (seg / n_group)
   int epl;     // experts per lane in the wave path (E / seg)
   int nbuf;    // LDS row buffers per segment (2 when a wave takes several rounds)
   int stage_bytes;  // bytes of one staged logits row (0: rows are read straight from HBM)
@@ -274,7 +276,11 @@ __device__ __forceinline__ void sig_off2(uint32_t d, uint32_t& o0, uint32_t& o1)
   o0 = v & 0xFFFFu;
   o1 = v >> 16;
 }
-__device__ __forceinline__ float sig_lds(uint32_t off) { return *reinterpret_cast<const float*>(g_lds + off); }
+// The table sits at LDS address 0 (the kernels that use it have no static
+// LDS, so their dynamic LDS starts there; the host checks this), which lets
+// the byte offset serve directly as the LDS address.
+typedef __attribute__((address_space(3))) const float* lds_cfloat_ptr;
+__device__ __forceinline__ float sig_lds(uint32_t off) { return *reinterpret_cast<lds_cfloat_ptr>((size_t)off); }
 
 // ----------------------------------------------------------------------------
 // Wave-level helpers (wave64, DPP row shifts and broadcasts).
@@ -539,6 +545,12 @@ __device__ void exact_token_wg(const Args& a, const Lds& L, int t, int tl, int* 
 // ----------------------------------------------------------------------------
 // s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N), N < 64
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -546,11 +558,17 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Copy the rows of the tokens of a wave (one per segment, token < 0 = none)
+// Copy the rows of the tokens of a wave (one per segment, token < 0 = none:
+// row 0 is copied in its place, so every call issues the same instructions)
 // from HBM into per-segment LDS buffers with gfx950's global_load_lds_dwordx4
 // (no VGPRs in flight).  Lane l writes LDS at base + 16*l, so the base for a
-// segment's instruction is shifted back by its first lane.
-template <int SEG>
+// segment's instruction is shifted back by its first lane.  With EPL known the
+// wave issues exactly row_dma_count<SEG, EPL, SZ>() instructions.
+template <int SEG, int EPL, int SZ>
+constexpr int row_dma_count() {
+  return (kWave / SEG) * ((EPL * SZ + 15) / 16);
+}
+template <int SEG, int EPL>
 __device__ __forceinline__ void stage_rows_async(const Args& a, unsigned char* buf, int stage_bytes, int tok,
                                                  int sz) {
   constexpr int NSEG = kWave / SEG;
@@ -558,13 +576,16 @@ __device__ __forceinline__ void stage_rows_async(const Args& a, unsigned char* b
   const int seg = lane / SEG;
   const int ls = lane % SEG;
   const int chunks = (a.E * sz) >> 4;
+  const int jn = EPL > 0 ? (EPL * sz + 15) / 16 : (chunks + SEG - 1) / SEG;  // instructions per segment
   const unsigned char* src = reinterpret_cast<const unsigned char*>(a.logits) + (size_t)(tok < 0 ? 0 : tok) * a.E * sz;
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
     unsigned char* dst = buf + (size_t)s * stage_bytes - (size_t)s * SEG * 16;  // >= 0: buffers start past 1 KiB
-    for (int j = 0; j * SEG < chunks; ++j) {
+#pragma unroll
+    for (int j = 0; j < (EPL > 0 ? (EPL * 4 + 15) / 16 : 64); ++j) {
+      if (j >= jn) break;
       const int c = j * SEG + ls;
-      if (seg == s && tok >= 0 && c < chunks)
+      if (seg == s && c < chunks)
         __builtin_amdgcn_global_load_lds(src + (size_t)c * 16,
                                          (__attribute__((address_space(3))) void*)(dst + j * SEG * 16), 16, 0, 0);
     }
@@ -860,6 +881,211 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   return status;
 }
 
+// One token per segment for BF16 logits.  Every key is exact (sigmoid from the
+// LDS table), so one pass decides the token: no margins and no redo.  Written
+// for a short instruction stream: compile-time layout, table offsets with
+// packed 16-bit arithmetic, straight-line group and threshold stages.
+template <int SEG, int EPL, int MODE>
+__device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, int t, int tl,
+                                         const unsigned char* stage, const float* bv) {
+  constexpr int NSEG = kWave / SEG;
+  constexpr int EPLM = EPL > 0 ? EPL : 64;
+  using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  const int seg = NSEG == 1 ? 0 : (lane >> 5);
+  const int ls = lane & (SEG - 1);
+  const int epl = EPL > 0 ? EPL : a.epl;
+  const int e0 = ls * epl;
+  const size_t row = (size_t)(act ? t : 0) * a.E;
+  // lanes of segment 1 (32-lane segments): the upper half of the wave
+  const unsigned long long seg1 = NSEG == 1 ? 0ull : 0xFFFFFFFF00000000ull;
+
+  // ---- 1. keys and lane top-2 ----
+  float av[EPLM];
+  float lm = -INFINITY, l2 = -INFINITY;
+  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.bias[e0 + i]; };
+  auto put_key = [&](int i, float key) {
+    av[i] = key;
+    l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
+    lm = fmaxf(lm, key);
+  };
+  auto put_pair = [&](int i, uint32_t d) {  // experts i, i+1 packed in d
+    uint32_t o0, o1;
+    sig_off2(d, o0, o1);
+    put_key(i, sig_lds(o0) + bias_of(i));
+    put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
+  };
+  if (EPL == 0) {  // slots past epl stay defined (their candidate bits are masked off)
+#pragma unroll
+    for (int i = 0; i < EPLM; ++i) av[i] = 0.0f;
+  }
+  {  // an idle segment's buffer holds a valid row too (row 0), so no branch here
+    if constexpr (MODE == LOAD_STAGE) {
+      if (EPL > 0 ? (EPL % 2 == 0) : (epl % 2 == 0)) {  // the lane run is 4-byte aligned
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(stage + e0 * 2);
+#pragma unroll
+        for (int j = 0; j < EPLM / 2; ++j)
+          if (2 * j < epl) put_pair(2 * j, s32[j]);
+      } else {
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
+#pragma unroll
+        for (int i = 0; i < EPLM; ++i)
+          if (i < epl) put_key(i, sig_lds(sig_off1(s16[i])) + bias_of(i));
+      }
+    } else {  // lane run is a whole number of 16-byte vectors
+      static_assert(EPLM < 8 || EPLM % 8 == 0, "vector width");
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
+                                                       (row + e0) * 2);
+#pragma unroll
+      for (int q = 0; q < (EPLM >= 8 ? EPLM / 8 : 0); ++q) {
+        if (q * 8 < epl) {
+          const uint4 v = src[q];
+          put_pair(q * 8 + 0, v.x);
+          put_pair(q * 8 + 2, v.y);
+          put_pair(q * 8 + 4, v.z);
+          put_pair(q * 8 + 6, v.w);
+        }
+      }
+    }
+  }
+
+  // ---- 2. group stage ----
+  bool allowed = act;
+  if (a.gstage) {
+    float g1 = lm, g2 = l2;
+#pragma unroll
+    for (int lev = 0; lev < (SEG == 64 ? 5 : 4); ++lev) {
+      if (lev < a.lg_lpg) {  // wave-uniform
+        const float p1 = butterfly_partner(g1, lev);
+        const float p2 = butterfly_partner(g2, lev);
+        const float n2 = fmaxf(fminf(g1, p1), fmaxf(g2, p2));
+        g1 = fmaxf(g1, p1);
+        g2 = n2;
+      }
+    }
+    const uint32_t gsu = f2s(g1 + g2);
+    const int g = ls >> a.lg_lpg;
+    const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
+    unsigned long long* gc = L.gcomp + w * kWave + seg * SEG;
+    if ((ls & ((1 << a.lg_lpg) - 1)) == 0) gc[g] = cg;
+    wave_sync_lds();
+    int rank = 0;
+    for (int h = 0; h < a.n_group; h += 2) {  // n_group is even here
+      const unsigned long long c0 = gc[h], c1 = gc[h + 1];
+      rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
+    }
+    allowed = act && rank < a.topk_group;
+    wave_sync_lds();  // every lane has read the composites before step 5 reuses the space
+  }
+
+  // ---- 3. threshold: k-th largest of the kept lanes' two largest keys ----
+  // At least k keys reach it, so every key of the exact top k does.
+  const bool two = EPLM >= 2 && (EPL > 0 || epl >= 2);
+  const uint32_t u1 = allowed ? f2s(lm) : 0u;
+  const uint32_t u2 = (allowed && two) ? f2s(l2) : 0u;
+  const unsigned long long ab = __ballot(allowed);
+  const uint32_t vmax = seg_max_u32<SEG>(u1);
+  const uint32_t vmin = seg_min_u32<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
+  uint32_t Ts[NSEG], bs[NSEG];
+  int okseg[NSEG];
+#pragma unroll
+  for (int q = 0; q < NSEG; ++q) {
+    const uint32_t hi = readlane(vmax, q * SEG), lo = readlane(vmin, q * SEG);
+    const int nval = (int)__popcll(seg_bits<SEG>(ab, q)) * (two ? 2 : 1);
+    okseg[q] = nval >= a.k;
+    const int top = (lo >= hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
+    Ts[q] = top < 0 ? min(hi, lo) : (hi & ~((2u << top) - 1u));  // every value counted is >= Ts
+    bs[q] = top < 0 ? 0u : (1u << top);
+  }
+  constexpr int kSteps = 10;  // resolve the 10 highest differing bits
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+#pragma unroll
+    for (int q = 0; q < NSEG; ++q) {
+      const uint32_t c = Ts[q] | bs[q];
+      const int n = (int)(__popcll(seg_bits<SEG>(__ballot(u1 >= c), q)) + __popcll(seg_bits<SEG>(__ballot(u2 >= c), q)));
+      Ts[q] = n >= a.k ? c : Ts[q];
+      bs[q] >>= 1;
+    }
+  }
+  const uint32_t T = (NSEG == 1 || seg == 0) ? Ts[0] : Ts[NSEG - 1];
+  const float thr = s2f(T);
+  const bool ok = (NSEG == 1 || seg == 0) ? okseg[0] : okseg[NSEG - 1];
+  int status = !act ? TOK_ESCALATE : (ok ? TOK_DONE : TOK_ESCALATE);
+
+  // ---- 4. candidates (keys >= thr), compacted in expert order ----
+  // The sign of key - thr is 1 exactly when key < thr (keys are never -0 and a
+  // nonzero difference never rounds to zero); alignbit shifts it into the mask.
+  uint32_t below_lo = 0, below_hi = 0;
+#pragma unroll
+  for (int i = EPLM - 1; i >= 0; --i) {
+    const uint32_t d = __float_as_uint(av[i] - thr);
+    if (i >= 32) below_hi = __builtin_amdgcn_alignbit(below_hi, d, 31);
+    else below_lo = __builtin_amdgcn_alignbit(below_lo, d, 31);
+  }
+  MaskT cm;
+  if constexpr (EPLM > 32)
+    cm = ~(((unsigned long long)below_hi << 32) | below_lo) & (epl >= 64 ? ~0ull : ((1ull << epl) - 1ull));
+  else
+    cm = ~below_lo & (EPLM == 32 ? 0xFFFFFFFFu : ((1u << (EPL > 0 ? EPL : epl)) - 1u));
+  if (!allowed || status != TOK_DONE) cm = 0;
+  const int mine = (int)__popcll((unsigned long long)cm);
+  const int incl = seg_incl_scan<SEG>(mine);
+  const int total = (int)seg_bcast<SEG>((uint32_t)incl);
+  if (status == TOK_DONE && total > SEG) status = TOK_ESCALATE;
+  int* ci = L.cand_i + w * kWave + seg * SEG;
+  if (status == TOK_DONE) {
+    int slot = incl - mine;
+    while (cm) {
+      const int i = (int)__builtin_ctzll((unsigned long long)cm);
+      ci[slot++] = e0 + i;
+      cm &= cm - 1;
+    }
+  }
+  wave_sync_lds();
+
+  // ---- 5. ranks of the candidates by (key desc, index asc) ----
+  const bool has = status == TOK_DONE && ls < total;
+  const int ce = has ? ci[ls] : 0;
+  float sf = 0.0f;
+  unsigned long long mykey = 0ull;  // below every real key
+  if (has) {
+    uint32_t h;
+    if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
+    else h = reinterpret_cast<const uint16_t*>(a.logits)[row + ce];
+    sf = sig_lds(sig_off1(h));
+    mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
+  }
+  unsigned long long* cc = L.cand_c + w * kWave + seg * SEG;
+  cc[ls] = mykey;
+  wave_sync_lds();
+  const int tot_ok = status == TOK_DONE ? total : 0;
+  int tmax = (int)readlane((uint32_t)tot_ok, 0);
+  if (NSEG == 2) tmax = max(tmax, (int)readlane((uint32_t)tot_ok, SEG));
+  int rank = 0;
+  for (int j = 0; j < tmax; j += 2) {
+    const unsigned long long c0 = cc[j], c1 = cc[j + 1];
+    rank += (c0 > mykey ? 1 : 0) + (c1 > mykey ? 1 : 0);
+  }
+  const bool sel = has && rank < a.k;
+
+  // ---- 6. outputs in expert order; weights s / sum(s), the sum in float64 ----
+  const unsigned long long sb = __ballot(sel) & (NSEG == 1 ? ~0ull : (seg ? seg1 : ~seg1));
+  const int pos = (int)__popcll(sb & ((1ull << lane) - 1ull));
+  const double ssum = seg_sum_d<SEG>(sel ? (double)sf : 0.0);
+  // |error| <= 2^-24 (sum to FP32) + 2^-23 (rcp) + 2^-24 (product), relative
+  const float rs = __builtin_amdgcn_rcpf((float)ssum);
+  if (sel) {
+    a.out_ids[(size_t)t * a.k + pos] = ce;
+    a.out_w[(size_t)t * a.k + pos] = sf * rs;
+    atomicOr(&L.bits[ce], 1ull << tl);
+    L.ids[tl * a.k + pos] = ce;
+  }
+  wave_sync_lds();
+  return status;
+}
+
 // Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets
 // and the per-token expert lists in LDS.  Wave w, round it takes tokens
 // (it*kNW + w)*NSEG + segment.
@@ -874,17 +1100,16 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   const int sb = a.stage_bytes;
   unsigned char* stg = L.stage + (size_t)w * a.nbuf * NSEG * sb;
   auto tok_of = [&](int it) { const int tl = (it * kNW + w) * NSEG + seg; return tl < nt ? tl : -1; };
-  if (a.fast && MODE == LOAD_STAGE) {
-    const int tl = tok_of(0);
-    stage_rows_async<SEG>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
-  }
-  // sigmoid table and bias into LDS by DMA, in flight together with the rows
+  // DMA into LDS: the sigmoid table (at LDS address 0) and the bias first, then
+  // this wave's first rows, so that a wave can wait for the shared data while
+  // its own rows are still in flight
   const int wbase = w * kWave * 16;  // LDS bytes of the lanes before this wave in one pass
   if (a.tbl) {
     const unsigned char* src = reinterpret_cast<const unsigned char*>(g_sig_table);
+#pragma unroll
     for (int j = 0; j * kWG * 16 < kSigBytes; ++j)
       __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
-                                       (__attribute__((address_space(3))) void*)(g_lds + j * kWG * 16 + wbase), 16,
+                                       (__attribute__((address_space(3))) void*)(size_t)(j * kWG * 16 + wbase), 16,
                                        0, 0);
   }
   if (a.bias_dma) {
@@ -897,12 +1122,22 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
                                          (__attribute__((address_space(3))) void*)(dst + j * kWG * 16 + wbase), 16,
                                          0, 0);
   }
+  if (a.fast && MODE == LOAD_STAGE) {
+    const int tl = tok_of(0);
+    stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
+  }
   for (int e = tid; e < a.E; e += kWG) {
     L.bits[e] = 0ull;
     if (!a.bias_dma) L.bias[e] = a.bias[e];
   }
   if (tid == 0) L.misc[0] = 0;
-  if (a.tbl || a.bias_dma) wait_vmem_all();  // this wave's DMA has landed (rows included)
+  if (a.tbl || a.bias_dma) {
+    // loads complete in order: with R row copies issued after the shared
+    // data, vmcnt <= R means the table and bias copies of this wave are done
+    constexpr int R = EPL > 0 ? row_dma_count<SEG, EPL, BF16 ? 2 : 4>() : 0;
+    if (a.fast && MODE == LOAD_STAGE && R > 0) wait_vmem_upto<R>();
+    else wait_vmem_all();
+  }
   __syncthreads();
   if (a.fast) {
     const int epl = EPL > 0 ? EPL : a.epl;
@@ -933,10 +1168,18 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         // the host gives two buffers whenever a wave has a next round
         if (a.nbuf > 1 && ((it + 1) * kNW + w) * NSEG < nt) {
           const int tn = tok_of(it + 1);
-          stage_rows_async<SEG>(a, stg + (size_t)(cb ^ 1) * NSEG * sb, sb, tn < 0 ? -1 : t0 + tn, BF16 ? 2 : 4);
+          stage_rows_async<SEG, EPL>(a, stg + (size_t)(cb ^ 1) * NSEG * sb, sb, tn < 0 ? -1 : t0 + tn, BF16 ? 2 : 4);
         }
       }
       const bool act = tl >= 0;
+      if constexpr (BF16) {
+        const int st = tbl_token<SEG, EPL, MODE>(a, L, act, t0 + tl, tl, cur, bv);
+        if (act && st == TOK_ESCALATE && ls == 0) {
+          const int q = atomicAdd(&L.misc[0], 1);
+          L.esc[q] = tl;
+        }
+        continue;
+      }
       int st = seg_token<SEG, EPL, BF16, MODE>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
       if (__ballot(act && st == TOK_REDO_EXACT)) {
         const bool redo = act && st == TOK_REDO_EXACT;
@@ -1294,6 +1537,20 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_table_ready[kMaxDevices];
 std::mutex g_table_mu;
 
+// Kernels that read the sigmoid table address it at LDS address 0, which
+// holds when they have no static LDS (their dynamic LDS then starts at 0).
+bool no_static_lds(const void* fn) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, bool> known;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = known.find(fn);
+  if (it != known.end()) return it->second;
+  hipFuncAttributes attr{};
+  const bool ok = hipFuncGetAttributes(&attr, fn) == hipSuccess && attr.sharedSizeBytes == 0;
+  known.emplace(fn, ok);
+  return ok;
+}
+
 int ensure_sig_table(hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRS_ERR_LAUNCH;
@@ -1418,6 +1675,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
       if (pl.total > kLdsLimit) continue;
       a.fast = 1;
       a.seg = seg;
+      a.lg_lpg = 31 - __builtin_clz((unsigned)(seg / n_group));
       a.epl = epl;
       a.stage_bytes = sb;
       a.nbuf = nbuf;
@@ -1446,8 +1704,9 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.nwg = 1;
     const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
     void* params[] = {&a};
-    return launch(reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode)), 1, kWG, lds, st, params,
-                  tm);
+    const void* fn = reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode));
+    if (a.tbl && !no_static_lds(fn)) return MRS_ERR_LAUNCH;
+    return launch(fn, 1, kWG, lds, st, params, tm);
   }
   a.tw = choose_tw(M);
   a.nwg = (M + a.tw - 1) / a.tw;
@@ -1465,8 +1724,9 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k, 0).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   void* p_one[] = {&a};
-  int rc = launch(reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode)), a.nwg, kWG, lds_sel, st,
-                  p_one, tm);
+  const void* fsel = reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode));
+  if (a.tbl && !no_static_lds(fsel)) return MRS_ERR_LAUNCH;
+  int rc = launch(fsel, a.nwg, kWG, lds_sel, st, p_one, tm);
   if (rc == MRS_OK)
     rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, kWG, 0, st, p_one, tm);
   if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, tm);
