@@ -101,7 +101,7 @@ struct Args {
 // LDS plan shared by host (size) and device (carving).
 // ----------------------------------------------------------------------------
 struct LdsPlan {
-  size_t sig, bits, redd, off, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
+  size_t sig, bits, redd, off, cpre, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
 __host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes) {
@@ -117,6 +117,7 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
   if (kind != KIND_SCATTER) p.bits = take((size_t)E * 8);
   p.redd = take((size_t)kNW * 8);
   if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
+  if (kind == KIND_SCATTER) p.cpre = take((size_t)E * 8);  // column prefixes, then counts
   if (kind != KIND_SCATTER) {
     p.ids = take((size_t)tw * k * 4);
     p.bias = take((size_t)E * 4);
@@ -144,6 +145,7 @@ struct Lds {
   unsigned long long* bits;
   double* redd;
   int* off;
+  int* cpre;
   int* ids;
   float* bias;
   int* cand_i;
@@ -167,6 +169,7 @@ __device__ inline Lds carve(int kind, const Args& a) {
   L.bits = reinterpret_cast<unsigned long long*>(g_lds + p.bits);
   L.redd = reinterpret_cast<double*>(g_lds + p.redd);
   L.off = reinterpret_cast<int*>(g_lds + p.off);
+  L.cpre = reinterpret_cast<int*>(g_lds + p.cpre);
   L.ids = reinterpret_cast<int*>(g_lds + p.ids);
   L.bias = reinterpret_cast<float*>(g_lds + p.bias);
   L.cand_i = reinterpret_cast<int*>(g_lds + p.cand_i);
@@ -957,11 +960,12 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
 #pragma unroll
     for (int lev = 0; lev < (SEG == 64 ? 5 : 4); ++lev) {
       if (lev < a.lg_lpg) {  // wave-uniform
+        // merge two (largest, second largest) pairs: the new second largest is
+        // the median of both largest values and the larger second value
         const float p1 = butterfly_partner(g1, lev);
         const float p2 = butterfly_partner(g2, lev);
-        const float n2 = fmaxf(fminf(g1, p1), fmaxf(g2, p2));
+        g2 = __builtin_amdgcn_fmed3f(g1, p1, fmaxf(g2, p2));
         g1 = fmaxf(g1, p1);
-        g2 = n2;
       }
     }
     const uint32_t gsu = f2s(g1 + g2);
@@ -987,18 +991,23 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
   const unsigned long long ab = __ballot(allowed);
   const uint32_t vmax = seg_max_u32<SEG>(u1);
   const uint32_t vmin = seg_min_u32<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
+  // lower end of the search: the smallest kept lane maximum when there are at
+  // least k kept lanes (every lane maximum reaches it), else the smallest value
+  const uint32_t vmin1 = seg_min_u32<SEG>(allowed ? u1 : 0xFFFFFFFFu);
   uint32_t Ts[NSEG], bs[NSEG];
   int okseg[NSEG];
 #pragma unroll
   for (int q = 0; q < NSEG; ++q) {
-    const uint32_t hi = readlane(vmax, q * SEG), lo = readlane(vmin, q * SEG);
-    const int nval = (int)__popcll(seg_bits<SEG>(ab, q)) * (two ? 2 : 1);
+    const int nal = (int)__popcll(seg_bits<SEG>(ab, q));
+    const uint32_t hi = readlane(vmax, q * SEG);
+    const uint32_t lo = nal >= a.k ? readlane(vmin1, q * SEG) : readlane(vmin, q * SEG);
+    const int nval = nal * (two ? 2 : 1);
     okseg[q] = nval >= a.k;
     const int top = (lo >= hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
     Ts[q] = top < 0 ? min(hi, lo) : (hi & ~((2u << top) - 1u));  // every value counted is >= Ts
     bs[q] = top < 0 ? 0u : (1u << top);
   }
-  constexpr int kSteps = 10;  // resolve the 10 highest differing bits
+  constexpr int kSteps = 9;  // resolve the 9 highest differing bits
 #pragma unroll
   for (int j = 0; j < kSteps; ++j) {
 #pragma unroll
@@ -1064,9 +1073,9 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
   int tmax = (int)readlane((uint32_t)tot_ok, 0);
   if (NSEG == 2) tmax = max(tmax, (int)readlane((uint32_t)tot_ok, SEG));
   int rank = 0;
-  for (int j = 0; j < tmax; j += 2) {
-    const unsigned long long c0 = cc[j], c1 = cc[j + 1];
-    rank += (c0 > mykey ? 1 : 0) + (c1 > mykey ? 1 : 0);
+  for (int j = 0; j < tmax; j += 4) {  // entries past total hold 0 (below every key)
+    const unsigned long long c0 = cc[j], c1 = cc[j + 1], c2 = cc[j + 2], c3 = cc[j + 3];
+    rank += (c0 > mykey ? 1 : 0) + (c1 > mykey ? 1 : 0) + (c2 > mykey ? 1 : 0) + (c3 > mykey ? 1 : 0);
   }
   const bool sel = has && rank < a.k;
 
@@ -1286,72 +1295,72 @@ __global__ __launch_bounds__(kWG) void k_select(Args a) {
 }
 
 // Launch 2: per expert, exclusive scan of its histogram column in workgroup
-// order (in place) and the padded total.  A block covers 8 experts; each of
-// its 64 row ranges is summed (rows kept in registers when a range has at
-// most 16 rows), the sums are scanned across in LDS, and the rows rewritten.
-constexpr int kColE = 8;
-constexpr int kColParts = kWG / kColE;
+// order (in place), the expert's total and its padded total.  A block covers
+// 64 experts with lane = expert, so every row access is one coalesced 256-byte
+// wave load; wave w owns a contiguous range of rows, kept in registers when
+// it has at most kColRegRows of them.
 constexpr int kColRegRows = 16;
 
 __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
-  __shared__ int part[kColParts][kColE];
-  const int ex = threadIdx.x % kColE;
-  const int pt = threadIdx.x / kColE;
-  const int e = blockIdx.x * kColE + ex;
+  __shared__ int part[kNW][kWave];
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  const int e = blockIdx.x * kWave + lane;
   const bool ok = e < a.E;
-  const int chunk = (a.nwg + kColParts - 1) / kColParts;
-  const int w0 = min(a.nwg, pt * chunk);
-  const int w1 = min(a.nwg, w0 + chunk);
+  const int rpw = (a.nwg + kNW - 1) / kNW;
+  const int r0 = min(a.nwg, w * rpw);
+  const int r1 = min(a.nwg, r0 + rpw);
   int32_t* col = a.ws_hist + (ok ? e : 0);
   const size_t stride = (size_t)a.E;
-  const bool inreg = chunk <= kColRegRows;
+  const bool inreg = rpw <= kColRegRows;
   int v[kColRegRows];
   int s = 0;
   if (inreg) {
 #pragma unroll
     for (int r = 0; r < kColRegRows; ++r) {
-      v[r] = (ok && w0 + r < w1) ? col[(size_t)(w0 + r) * stride] : 0;
+      v[r] = (ok && r0 + r < r1) ? col[(size_t)(r0 + r) * stride] : 0;
       s += v[r];
     }
   } else if (ok) {
-#pragma unroll 8
-    for (int w = w0; w < w1; ++w) s += col[(size_t)w * stride];
+    for (int r = r0; r < r1; ++r) s += col[(size_t)r * stride];
   }
-  part[pt][ex] = s;
+  part[w][lane] = s;
   __syncthreads();
   int pre = 0, total = 0;
-  for (int q = 0; q < kColParts; ++q) {
-    const int x = part[q][ex];
-    pre += q < pt ? x : 0;
+#pragma unroll
+  for (int q = 0; q < kNW; ++q) {
+    const int x = part[q][lane];
+    pre += q < w ? x : 0;
     total += x;
   }
   if (!ok) return;
   if (inreg) {
 #pragma unroll
     for (int r = 0; r < kColRegRows; ++r) {
-      if (w0 + r < w1) {
-        col[(size_t)(w0 + r) * stride] = pre;
+      if (r0 + r < r1) {
+        col[(size_t)(r0 + r) * stride] = pre;
         pre += v[r];
       }
     }
   } else {
-#pragma unroll 8
-    for (int w = w0; w < w1; ++w) {
-      const int x = col[(size_t)w * stride];
-      col[(size_t)w * stride] = pre;
+    for (int r = r0; r < r1; ++r) {
+      const int x = col[(size_t)r * stride];
+      col[(size_t)r * stride] = pre;
       pre += x;
     }
   }
-  if (pt == 0) {
+  if (w == 0) {
     a.ws_tot[e] = total;
     a.ws_pad[e] = pad_up(total, a.block);
   }
 }
 
 // Launch 3: expert offsets, padding, expert_of_block and the stable scatter.
-// The slot records are loaded before the offset scan so the two global reads
-// overlap.
+// Everything the block reads from the workspace (its slot records, the padded
+// totals, its row of column prefixes, the counts of the experts whose padding
+// it writes) is requested up front, so the block waits for one round trip.
 constexpr int kRecPerThread = (kTwMax * 64 + kWG - 1) / kWG;
+constexpr int kEPerThread = kEMax / kWG;
 
 __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   const Lds L = carve(KIND_SCATTER, a);
@@ -1361,31 +1370,62 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   const int nt = min(a.tw, a.M - t0);
   const int ns = nt * a.k;
   const int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
-  int rv[kRecPerThread];
+  const int32_t* colpre = a.ws_hist + (size_t)w * a.E;
+  const int ept = (a.E + kWG - 1) / kWG;  // experts per thread in the offset scan (contiguous)
+  const int es0 = (int)((int64_t)w * a.E / a.nwg);
+  const int es1 = (int)((int64_t)(w + 1) * a.E / a.nwg);
+  int rv[kRecPerThread], pv[kEPerThread], cv[kEPerThread], tv[kEPerThread];
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
     const int q = tid + j * kWG;
     rv[j] = q < ns ? rec[q] : 0;
   }
-  const int total = expert_offsets(a, L, [&](int e) { return a.ws_pad[e]; });
+#pragma unroll
+  for (int i = 0; i < kEPerThread; ++i) {
+    const int e = tid * ept + i;
+    pv[i] = (i < ept && e < a.E) ? a.ws_pad[e] : 0;
+    const int e2 = tid + i * kWG;
+    cv[i] = e2 < a.E ? colpre[e2] : 0;
+    tv[i] = es0 + e2 < es1 ? a.ws_tot[es0 + e2] : 0;  // counts of the experts this block pads
+  }
+  int* cnt = L.cpre + a.E;
+#pragma unroll
+  for (int i = 0; i < kEPerThread; ++i) {
+    const int e2 = tid + i * kWG;
+    if (e2 < a.E) L.cpre[e2] = cv[i];
+    if (es0 + e2 < es1) cnt[e2] = tv[i];
+  }
+  // exclusive scan of the padded totals over all experts
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < kEPerThread; ++i) local += pv[i];
+  int pre = wg_excl_scan(L, local);
+#pragma unroll
+  for (int i = 0; i < kEPerThread; ++i) {
+    const int e = tid * ept + i;
+    if (i < ept && e < a.E) {
+      L.off[e] = pre;
+      pre += pv[i];
+    }
+  }
+  if (tid == kWG - 1) L.misc[1] = pre;
+  __syncthreads();
+  const int total = L.misc[1];
   if (w == 0 && tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
-  const int es0 = (int)((int64_t)w * a.E / a.nwg);
-  const int es1 = (int)((int64_t)(w + 1) * a.E / a.nwg);
   for (int e = es0; e < es1; ++e) {
-    const int c = a.ws_tot[e];
-    const int p = a.ws_pad[e];
+    const int c = cnt[e - es0];
     const int o = L.off[e];
+    const int p = (e + 1 < a.E ? L.off[e + 1] : total) - o;
     for (int r = c + tid; r < p; r += kWG) a.sorted_ids[o + r] = sentinel;
     for (int b = tid; b < p / a.block; b += kWG) a.eob[o / a.block + b] = e;
   }
-  const int32_t* colpre = a.ws_hist + (size_t)w * a.E;
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
     const int q = tid + j * kWG;
     if (q < ns) {
       const int e = rv[j] & 0xFFFF;
-      a.sorted_ids[L.off[e] + colpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
+      a.sorted_ids[L.off[e] + L.cpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
     }
   }
 }
@@ -1728,7 +1768,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   if (a.tbl && !no_static_lds(fsel)) return MRS_ERR_LAUNCH;
   int rc = launch(fsel, a.nwg, kWG, lds_sel, st, p_one, tm);
   if (rc == MRS_OK)
-    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kColE - 1) / kColE, kWG, 0, st, p_one, tm);
+    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kWave - 1) / kWave, kWG, 0, st, p_one, tm);
   if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, tm);
   return rc;
 }
