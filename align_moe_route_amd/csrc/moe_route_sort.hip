@@ -73,6 +73,8 @@ struct Args {
   const void* logits;
   const float* bias;
   int M, E, k, n_group, topk_group, block;
+  uint32_t blk_sh;        // n / block == (n * blk_mul) >> blk_sh for 0 <= n < 2^31
+  unsigned long long blk_mul;
   int G;       // experts per group
   int seg;    // lanes per token in the wave path (32 or 64)
   int lg_lpg;  // log2 of the lanes per group in the wave path (seg / n_group)
@@ -84,6 +86,7 @@ struct Args {
   int fast;    // the wave layout covers this shape
   int tbl;     // BF16 logits: keys from the sigmoid table in LDS (exact)
   int bias_dma;  // bias is copied into LDS by DMA (16-byte aligned, E % 4 == 0)
+  int rows_first;  // issue the row copies before the shared data (latency-bound calls)
   int gstage;  // the group stage changes the result (1 < topk_group < n_group, G > 1)
   int32_t* out_ids;
   float* out_w;
@@ -203,8 +206,14 @@ __device__ __forceinline__ float next_down(float f) {
   else u = 0x80000001u;
   return __uint_as_float(u);
 }
-__device__ __forceinline__ int pad_up(int c, int block) {
-  return c == 0 ? 0 : ((c - 1) / block + 1) * block;
+// n / block for 0 <= n < 2^31 by multiply and shift: with l = ceil(log2 block),
+// mul = ceil(2^(31+l) / block) makes the error of n*mul/2^(31+l) below
+// n / 2^(31+l) < 1/block, so the floor is exact.
+__device__ __forceinline__ int div_block(int n, const Args& a) {
+  return (int)(((unsigned long long)(uint32_t)n * a.blk_mul) >> a.blk_sh);
+}
+__device__ __forceinline__ int pad_block(int c, const Args& a) {
+  return (c == 0) ? 0 : (div_block(c - 1, a) + 1) * a.block;
 }
 
 template <bool BF16>
@@ -1113,6 +1122,10 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   // this wave's first rows, so that a wave can wait for the shared data while
   // its own rows are still in flight
   const int wbase = w * kWave * 16;  // LDS bytes of the lanes before this wave in one pass
+  if (a.rows_first && a.fast && MODE == LOAD_STAGE) {
+    const int tl = tok_of(0);
+    stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
+  }
   if (a.tbl) {
     const unsigned char* src = reinterpret_cast<const unsigned char*>(g_sig_table);
 #pragma unroll
@@ -1131,7 +1144,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
                                          (__attribute__((address_space(3))) void*)(dst + j * kWG * 16 + wbase), 16,
                                          0, 0);
   }
-  if (a.fast && MODE == LOAD_STAGE) {
+  if (!a.rows_first && a.fast && MODE == LOAD_STAGE) {
     const int tl = tok_of(0);
     stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
   }
@@ -1144,7 +1157,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     // loads complete in order: with R row copies issued after the shared
     // data, vmcnt <= R means the table and bias copies of this wave are done
     constexpr int R = EPL > 0 ? row_dma_count<SEG, EPL, BF16 ? 2 : 4>() : 0;
-    if (a.fast && MODE == LOAD_STAGE && R > 0) wait_vmem_upto<R>();
+    if (!a.rows_first && a.fast && MODE == LOAD_STAGE && R > 0) wait_vmem_upto<R>();
     else wait_vmem_all();
   }
   __syncthreads();
@@ -1256,15 +1269,15 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
   select_tokens<SEG, EPL, BF16, MODE>(a, L, 0, a.M);
   const int tid = threadIdx.x;
-  const int total = expert_offsets(a, L, [&](int e) { return pad_up(__popcll(L.bits[e]), a.block); });
+  const int total = expert_offsets(a, L, [&](int e) { return pad_block(__popcll(L.bits[e]), a); });
   if (tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
   for (int e = tid; e < a.E; e += kWG) {
     const int c = __popcll(L.bits[e]);
-    const int p = pad_up(c, a.block);
+    const int p = pad_block(c, a);
     const int o = L.off[e];
     for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
-    for (int b = o / a.block; b < (o + p) / a.block; ++b) a.eob[b] = e;
+    for (int b = div_block(o, a); b < div_block(o + p, a); ++b) a.eob[b] = e;
   }
   for (int q = tid; q < sentinel; q += kWG) {
     const int tl = q / a.k;
@@ -1351,7 +1364,7 @@ __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
   }
   if (w == 0) {
     a.ws_tot[e] = total;
-    a.ws_pad[e] = pad_up(total, a.block);
+    a.ws_pad[e] = pad_block(total, a);
   }
 }
 
@@ -1418,7 +1431,8 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
     const int o = L.off[e];
     const int p = (e + 1 < a.E ? L.off[e + 1] : total) - o;
     for (int r = c + tid; r < p; r += kWG) a.sorted_ids[o + r] = sentinel;
-    for (int b = tid; b < p / a.block; b += kWG) a.eob[o / a.block + b] = e;
+    const int b0 = div_block(o, a), nb = div_block(p, a);
+    for (int b = tid; b < nb; b += kWG) a.eob[b0 + b] = e;
   }
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
@@ -1681,6 +1695,12 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   a.n_group = n_group;
   a.topk_group = topk_group;
   a.block = block;
+  {
+    uint32_t l = 0;
+    while ((1ull << l) < (unsigned long long)block) ++l;
+    a.blk_sh = 31 + l;
+    a.blk_mul = ((1ull << (31 + l)) + (unsigned long long)block - 1) / (unsigned long long)block;
+  }
   a.G = E / n_group;
   a.gstage = (n_group > 1 && topk_group < n_group && a.G > 1) ? 1 : 0;
   a.out_ids = out_ids;
@@ -1742,6 +1762,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   if (want_small) {
     a.tw = M;
     a.nwg = 1;
+    a.rows_first = 1;
     const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
     void* params[] = {&a};
     const void* fn = reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode));

@@ -10,6 +10,11 @@ log-Zipf expert popularity).  To keep the logits out of the 256 MB last-level
 cache the timed loop rotates over distinct copies of the input totalling at
 least --rotate-mb megabytes.
 
+The timed loop replays a HIP graph of consecutive calls, so the per-call time
+is the GPU's (kernels and the gaps between them), not the Python launch
+overhead; the eager host wall time per call (launch + synchronise) is
+reported beside it for the small workloads.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import os
@@ -71,6 +76,11 @@ def to_gpu(inp, torch):
     return x, torch.from_numpy(inp.bias).cuda()
 
 
+def graph_size(steps, cap=64):
+    """Calls per captured graph: the largest divisor of `steps` not above `cap`."""
+    return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
+
+
 def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     inp = workloads.make_inputs(cfg)
     x0, b = to_gpu(inp, torch)
@@ -81,14 +91,25 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     xs = [x0] + [torch.roll(x0, shifts=(i * 997) % max(cfg.M, 1), dims=0).contiguous()
                  for i in range(1, nrot)]
     out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    torch.cuda.synchronize()
+    # The timed steps replay a HIP graph of G consecutive calls (rotating inputs),
+    # so host-side launch overhead does not pace the GPU.
+    G = graph_size(steps)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(G):
+            amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // G)):
+            graph.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(steps):
-        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    with torch.cuda.stream(stream):
+        for _ in range(steps // G):
+            graph.replay()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
