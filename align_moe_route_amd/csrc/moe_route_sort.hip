@@ -104,7 +104,7 @@ struct Args {
 // LDS plan shared by host (size) and device (carving).
 // ----------------------------------------------------------------------------
 struct LdsPlan {
-  size_t sig, bits, redd, off, cpre, ids, bias, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
+  size_t sig, bits, redd, off, cpre, ids, bias, biasT, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
 __host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes) {
@@ -124,6 +124,7 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
   if (kind != KIND_SCATTER) {
     p.ids = take((size_t)tw * k * 4);
     p.bias = take((size_t)E * 4);
+    p.biasT = take((size_t)E * 4);
     p.cand_i = take((size_t)kNW * kWave * 4);
     p.cand_c = take((size_t)kNW * kWave * 8);
     p.gcomp = p.cand_c;  // group composites (step 2) and candidate keys (step 5) of a wave never overlap
@@ -151,6 +152,7 @@ struct Lds {
   int* cpre;
   int* ids;
   float* bias;
+  float* biasT;  // bias[lane run i of lane l] at i * seg + l: conflict-free lane reads
   int* cand_i;
   unsigned long long* cand_c;
   unsigned long long* gcomp;
@@ -175,6 +177,7 @@ __device__ inline Lds carve(int kind, const Args& a) {
   L.cpre = reinterpret_cast<int*>(g_lds + p.cpre);
   L.ids = reinterpret_cast<int*>(g_lds + p.ids);
   L.bias = reinterpret_cast<float*>(g_lds + p.bias);
+  L.biasT = reinterpret_cast<float*>(g_lds + p.biasT);
   L.cand_i = reinterpret_cast<int*>(g_lds + p.cand_i);
   L.cand_c = reinterpret_cast<unsigned long long*>(g_lds + p.cand_c);
   L.gcomp = reinterpret_cast<unsigned long long*>(g_lds + p.gcomp);
@@ -696,7 +699,7 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
   // ---- 1. keys and lane top-2 ----
   float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
-  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.bias[e0 + i]; };
+  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.biasT[i * SEG + ls]; };
   auto put_key = [&](int i, float key) {
     av[i] = key;
     l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
@@ -739,11 +742,17 @@ __device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, 
       static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
                                                        (row + e0) * SZ);
+      // every vector load of the lane run is issued before the first use (a
+      // load past the run repeats the last vector, which stays inside the row)
+      constexpr int NQ = EPLM >= PER ? EPLM / PER : 0;
+      const int nq = epl / PER;
+      uint4 raw[NQ > 0 ? NQ : 1];
 #pragma unroll
-      for (int q = 0; q < (EPLM >= PER ? EPLM / PER : 0); ++q) {
-        if (q * PER < epl) {
-          const uint4 v = src[q];
-          const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q < nq) {
+          const uint32_t d[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if constexpr (BF16) put_pair(q * PER + 2 * j, d[j]);
@@ -916,7 +925,7 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
   // ---- 1. keys and lane top-2 ----
   float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
-  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.bias[e0 + i]; };
+  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.biasT[i * SEG + ls]; };
   auto put_key = [&](int i, float key) {
     av[i] = key;
     l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
@@ -949,14 +958,18 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
       static_assert(EPLM < 8 || EPLM % 8 == 0, "vector width");
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
                                                        (row + e0) * 2);
+      constexpr int NQ = EPLM >= 8 ? EPLM / 8 : 0;
+      const int nq = epl / 8;
+      uint4 raw[NQ > 0 ? NQ : 1];
 #pragma unroll
-      for (int q = 0; q < (EPLM >= 8 ? EPLM / 8 : 0); ++q) {
-        if (q * 8 < epl) {
-          const uint4 v = src[q];
-          put_pair(q * 8 + 0, v.x);
-          put_pair(q * 8 + 2, v.y);
-          put_pair(q * 8 + 4, v.z);
-          put_pair(q * 8 + 6, v.w);
+      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];  // all loads first
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q < nq) {
+          put_pair(q * 8 + 0, raw[q].x);
+          put_pair(q * 8 + 2, raw[q].y);
+          put_pair(q * 8 + 4, raw[q].z);
+          put_pair(q * 8 + 6, raw[q].w);
         }
       }
     }
@@ -1173,7 +1186,11 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         bmax = fmaxf(bmax, fabsf(bv[i]));
       }
     } else {
-      for (int i = 0; i < epl; ++i) bmax = fmaxf(bmax, fabsf(L.bias[e0 + i]));
+      // lanes read their biases from a transposed copy: lane runs of 64
+      // experts would put every lane of a wave on the same LDS bank
+      for (int e = tid; e < a.E; e += kWG) L.biasT[(e % epl) * SEG + e / epl] = L.bias[e];
+      __syncthreads();
+      for (int i = 0; i < epl; ++i) bmax = fmaxf(bmax, fabsf(L.biasT[i * SEG + ls]));
     }
     // Every segment covers all experts, so this is max |bias|.
     // |fast key - exact key| <= 2^-21 + rounding of both sums <= delta;
