@@ -671,244 +671,19 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
   return (bal >> (s * SEG)) & 0xFFFFFFFFull;
 }
 
-// One token per segment.  BF16 logits take their correctly rounded sigmoid
-// from the LDS table, so every key is exact from the start and the token is
-// decided in one pass.  FP32 logits rank with sigmoid_fast and a certified
-// margin (see the header comment); `exact` = the redo pass with correctly
-// rounded keys.
+// One token per segment (see the header comment).  BF16 logits take their
+// correctly rounded sigmoid from the LDS table, so every key is exact and one
+// pass decides the token.  FP32 logits rank with sigmoid_fast: the group
+// boundary is certified against the error of the fast scores (else the token
+// is redone with `exact` keys) and the candidate line is lowered by twice the
+// key error.  Written for a short instruction stream: compile-time layout,
+// table offsets with packed 16-bit arithmetic, straight-line group and
+// threshold stages.
 template <int SEG, int EPL, bool BF16, int MODE>
-__device__ __forceinline__ int seg_token(const Args& a, const Lds& L, bool act, int t, int tl,
-                                         const unsigned char* stage, const float* bv, double delta,
-                                         double epsg, bool exact) {
-  constexpr bool TBL = BF16;
-  constexpr int NSEG = kWave / SEG;
-  constexpr int EPLM = EPL > 0 ? EPL : 64;
-  using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
-  const int lane = lane_id();
-  const int w = threadIdx.x >> 6;
-  const int seg = lane / SEG;
-  const int ls = lane % SEG;
-  const int epl = EPL > 0 ? EPL : a.epl;
-  const int e0 = ls * epl;
-  const size_t row = (size_t)(act ? t : 0) * a.E;
-  constexpr int SZ = BF16 ? 2 : 4;
-  const unsigned long long below = (SEG == 64) ? ((1ull << lane) - 1ull) : ((1ull << ls) - 1ull);
-  int status = act ? TOK_DONE : TOK_ESCALATE;  // an idle segment writes nothing
-  if (TBL) exact = true;
-
-  // ---- 1. keys and lane top-2 ----
-  float av[EPLM];
-  float lm = -INFINITY, l2 = -INFINITY;
-  auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.biasT[i * SEG + ls]; };
-  auto put_key = [&](int i, float key) {
-    av[i] = key;
-    l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
-    lm = fmaxf(lm, key);
-  };
-  auto put = [&](int i, float x) {  // FP32 logits
-    put_key(i, (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i));
-    if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
-  };
-  auto put_pair = [&](int i, uint32_t d) {  // BF16 logits of experts i, i+1 packed in d
-    uint32_t o0, o1;
-    sig_off2(d, o0, o1);
-    put_key(i, sig_lds(o0) + bias_of(i));
-    put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
-  };
-#pragma unroll
-  for (int i = 0; i < EPLM; ++i) av[i] = -INFINITY;
-  if (act) {
-    if constexpr (MODE == LOAD_STAGE) {  // the row is already in this segment's LDS buffer
-      if constexpr (BF16) {
-        if (EPL > 0 ? (EPL % 2 == 0) : (epl % 2 == 0)) {  // the lane run is 4-byte aligned
-          const uint32_t* s32 = reinterpret_cast<const uint32_t*>(stage + e0 * 2);
-#pragma unroll
-          for (int j = 0; j < EPLM / 2; ++j)
-            if (2 * j < epl) put_pair(2 * j, s32[j]);
-        } else {
-          const uint16_t* s16 = reinterpret_cast<const uint16_t*>(stage) + e0;
-#pragma unroll
-          for (int i = 0; i < EPLM; ++i)
-            if (i < epl) put_key(i, sig_lds(sig_off1(s16[i])) + bias_of(i));
-        }
-      } else {
-        const float* s32 = reinterpret_cast<const float*>(stage) + e0;
-#pragma unroll
-        for (int i = 0; i < EPLM; ++i)
-          if (i < epl) put(i, s32[i]);
-      }
-    } else {  // lane run is 16-byte aligned and a multiple of 16 bytes
-      constexpr int PER = 16 / SZ;
-      static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                       (row + e0) * SZ);
-      // every vector load of the lane run is issued before the first use (a
-      // load past the run repeats the last vector, which stays inside the row)
-      constexpr int NQ = EPLM >= PER ? EPLM / PER : 0;
-      const int nq = epl / PER;
-      uint4 raw[NQ > 0 ? NQ : 1];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        if (q < nq) {
-          const uint32_t d[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (BF16) put_pair(q * PER + 2 * j, d[j]);
-            else put(q * PER + j, __uint_as_float(d[j]));
-          }
-        }
-      }
-    }
-  }
-
-  // ---- 2. group stage ----
-  bool allowed = act;
-  if (a.gstage) {
-    const int lpg = SEG / a.n_group;
-    float g1 = lm, g2 = l2;
-    for (int lev = 0; (1 << lev) < lpg; ++lev) {
-      const float p1 = butterfly_partner(g1, lev);
-      const float p2 = butterfly_partner(g2, lev);
-      const float n2 = fmaxf(fminf(g1, p1), fmaxf(g2, p2));
-      g1 = fmaxf(g1, p1);
-      g2 = n2;
-    }
-    const uint32_t gsu = f2s(g1 + g2);
-    const int g = ls / lpg;
-    const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
-    unsigned long long* gc = L.gcomp + w * kWave + seg * SEG;
-    if (ls % lpg == 0) gc[g] = cg;
-    wave_sync_lds();
-    int rank = 0;
-    for (int h = 0; h < a.n_group; ++h) rank += gc[h] > cg ? 1 : 0;
-    const bool keep = rank < a.topk_group;
-    if (!exact) {
-      // the kept groups' lowest score must beat the others' highest by more
-      // than the error of two fast group scores
-      const uint32_t kept_min = seg_min_u32<SEG>(keep ? gsu : 0xFFFFFFFFu);
-      const uint32_t drop_max = seg_max_u32<SEG>(keep ? 0u : gsu);
-      const double gap = (double)s2f(kept_min) - (double)s2f(drop_max);
-      if (act && !(gap > 2.0 * epsg)) status = TOK_REDO_EXACT;
-    }
-    allowed = act && keep;
-    wave_sync_lds();  // every lane has read the composites before step 5 reuses the space
-  }
-
-  // ---- 3. threshold: k-th largest of the kept lanes' two largest keys ----
-  // (at least k keys reach it: the exact top-k keys are all >= it with exact
-  // keys, >= it - 2 delta with fast keys)
-  constexpr int R = EPLM >= 2 ? 2 : 1;
-  const int nallow = (int)__popcll(seg_bits<SEG>(__ballot(allowed), seg));
-  if (status == TOK_DONE && nallow * (EPL == 1 || (EPL == 0 && epl < 2) ? 1 : R) < a.k) status = TOK_ESCALATE;
-  const bool two = R == 2 && (EPL > 0 || epl >= 2);
-  const uint32_t u1 = allowed ? f2s(lm) : 0u;
-  const uint32_t u2 = (allowed && two) ? f2s(l2) : 0u;
-  const uint32_t vmax = seg_max_u32<SEG>(u1);
-  const uint32_t vmin = seg_min_u32<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
-  uint32_t Ts[NSEG];
-  int tops[NSEG];
-#pragma unroll
-  for (int s = 0; s < NSEG; ++s) {
-    const uint32_t hi = readlane(vmax, s * SEG), lo = readlane(vmin, s * SEG);
-    tops[s] = (hi == lo || lo > hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
-    Ts[s] = tops[s] < 0 ? min(hi, lo) : (hi & ~((2u << tops[s]) - 1u));  // every value counted is >= Ts
-  }
-  constexpr int kSteps = 10;  // resolve the 10 highest differing bits
-  for (int j = 0; j < kSteps; ++j) {
-    uint32_t cs[NSEG];
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) cs[s] = (tops[s] - j >= 0) ? (Ts[s] | (1u << (tops[s] - j))) : Ts[s];
-    uint32_t c = cs[0];
-#pragma unroll
-    for (int s = 1; s < NSEG; ++s) c = seg == s ? cs[s] : c;
-    const unsigned long long m1 = __ballot(u1 >= c);
-    const unsigned long long m2 = __ballot(u2 >= c);
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-      const int n = (int)(__popcll(seg_bits<SEG>(m1, s)) + __popcll(seg_bits<SEG>(m2, s)));
-      if (n >= a.k) Ts[s] = cs[s];
-    }
-  }
-  uint32_t T = Ts[0];
-#pragma unroll
-  for (int s = 1; s < NSEG; ++s) T = seg == s ? Ts[s] : T;
-  float thr = s2f(T);
-  if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
-
-  // ---- 4. candidates, compacted in expert order ----
-  MaskT cm = 0;
-#pragma unroll
-  for (int i = EPLM - 1; i >= 0; --i) cm = cm + cm + ((i < epl && av[i] >= thr) ? 1 : 0);  // bit i = expert i
-  if (!allowed || status != TOK_DONE) cm = 0;
-  const int mine = (int)__popcll((unsigned long long)cm);
-  const int incl = seg_incl_scan<SEG>(mine);
-  const int total = (int)seg_bcast<SEG>((uint32_t)incl);
-  if (status == TOK_DONE && total > SEG) status = TOK_ESCALATE;
-  int* ci = L.cand_i + w * kWave + seg * SEG;
-  if (status == TOK_DONE) {
-    int slot = incl - mine;
-    while (cm) {
-      const int i = (int)__builtin_ctzll((unsigned long long)cm);
-      ci[slot++] = e0 + i;
-      cm &= cm - 1;
-    }
-  }
-  wave_sync_lds();
-
-  // ---- 5. exact keys of the candidates, ranks by (key desc, index asc) ----
-  const bool has = status == TOK_DONE && ls < total;
-  const int ce = has ? ci[ls] : 0;
-  float sf = 0.0f;
-  unsigned long long mykey = 0ull;  // below every real key
-  if (has) {
-    if constexpr (TBL) {
-      uint32_t h;
-      if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
-      else h = reinterpret_cast<const uint16_t*>(a.logits)[row + ce];
-      sf = sig_lds(sig_off1(h));
-    } else {
-      float x;
-      if constexpr (MODE == LOAD_STAGE) x = reinterpret_cast<const float*>(stage)[ce];
-      else x = load_logit<BF16>(a.logits, row + ce);
-      sf = sigmoid_exact(x);
-    }
-    mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
-  }
-  unsigned long long* cc = L.cand_c + w * kWave + seg * SEG;
-  cc[ls] = mykey;
-  wave_sync_lds();
-  int tmax = (int)readlane((uint32_t)(status == TOK_DONE ? total : 0), 0);
-#pragma unroll
-  for (int q = 1; q < NSEG; ++q) tmax = max(tmax, (int)readlane((uint32_t)(status == TOK_DONE ? total : 0), q * SEG));
-  int rank = 0;
-  for (int j = 0; j < tmax; j += 2) {
-    const unsigned long long c0 = cc[j], c1 = cc[j + 1];
-    rank += (c0 > mykey ? 1 : 0) + (c1 > mykey ? 1 : 0);
-  }
-  const bool sel = has && rank < a.k;
-
-  // ---- 6. outputs in expert order; weights s / sum(s), the sum in float64 ----
-  const int pos = (int)__popcll(seg_bits<SEG>(__ballot(sel), seg) & below);
-  const double ssum = seg_sum_d<SEG>(sel ? (double)sf : 0.0);
-  if (sel) {
-    a.out_ids[(size_t)t * a.k + pos] = ce;
-    a.out_w[(size_t)t * a.k + pos] = (float)((double)sf / ssum);
-    atomicOr(&L.bits[ce], 1ull << tl);
-    L.ids[tl * a.k + pos] = ce;
-  }
-  wave_sync_lds();
-  return status;
-}
-
-// One token per segment for BF16 logits.  Every key is exact (sigmoid from the
-// LDS table), so one pass decides the token: no margins and no redo.  Written
-// for a short instruction stream: compile-time layout, table offsets with
-// packed 16-bit arithmetic, straight-line group and threshold stages.
-template <int SEG, int EPL, int MODE>
-__device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, int t, int tl,
-                                         const unsigned char* stage, const float* bv) {
+__device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act, int t, int tl,
+                                          const unsigned char* stage, const float* bv, double delta,
+                                          double epsg, bool exact) {
+  if (BF16) exact = true;
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
   using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
@@ -931,18 +706,27 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
     l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
     lm = fmaxf(lm, key);
   };
-  auto put_pair = [&](int i, uint32_t d) {  // experts i, i+1 packed in d
+  auto put_pair = [&](int i, uint32_t d) {  // BF16 logits of experts i, i+1 packed in d
     uint32_t o0, o1;
     sig_off2(d, o0, o1);
     put_key(i, sig_lds(o0) + bias_of(i));
     put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
+  };
+  auto put = [&](int i, float x) {  // FP32 logit of expert i
+    put_key(i, (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i));
+    if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
   };
   if (EPL == 0) {  // slots past epl stay defined (their candidate bits are masked off)
 #pragma unroll
     for (int i = 0; i < EPLM; ++i) av[i] = 0.0f;
   }
   {  // an idle segment's buffer holds a valid row too (row 0), so no branch here
-    if constexpr (MODE == LOAD_STAGE) {
+    if constexpr (MODE == LOAD_STAGE && !BF16) {
+      const float* s32 = reinterpret_cast<const float*>(stage) + e0;
+#pragma unroll
+      for (int i = 0; i < EPLM; ++i)
+        if (i < epl) put(i, s32[i]);
+    } else if constexpr (MODE == LOAD_STAGE) {
       if (EPL > 0 ? (EPL % 2 == 0) : (epl % 2 == 0)) {  // the lane run is 4-byte aligned
         const uint32_t* s32 = reinterpret_cast<const uint32_t*>(stage + e0 * 2);
 #pragma unroll
@@ -955,21 +739,31 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
           if (i < epl) put_key(i, sig_lds(sig_off1(s16[i])) + bias_of(i));
       }
     } else {  // lane run is a whole number of 16-byte vectors
-      static_assert(EPLM < 8 || EPLM % 8 == 0, "vector width");
+      constexpr int PER = BF16 ? 8 : 4;  // logits per vector
+      static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                       (row + e0) * 2);
-      constexpr int NQ = EPLM >= 8 ? EPLM / 8 : 0;
-      const int nq = epl / 8;
+                                                       (row + e0) * (BF16 ? 2 : 4));
+      // every load of the lane run is issued before the first use (a load past
+      // the run repeats the last vector, which stays inside the row)
+      constexpr int NQ = EPLM >= PER ? EPLM / PER : 0;
+      const int nq = epl / PER;
       uint4 raw[NQ > 0 ? NQ : 1];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];  // all loads first
+      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if (q < nq) {
-          put_pair(q * 8 + 0, raw[q].x);
-          put_pair(q * 8 + 2, raw[q].y);
-          put_pair(q * 8 + 4, raw[q].z);
-          put_pair(q * 8 + 6, raw[q].w);
+          if constexpr (BF16) {
+            put_pair(q * 8 + 0, raw[q].x);
+            put_pair(q * 8 + 2, raw[q].y);
+            put_pair(q * 8 + 4, raw[q].z);
+            put_pair(q * 8 + 6, raw[q].w);
+          } else {
+            put(q * 4 + 0, __uint_as_float(raw[q].x));
+            put(q * 4 + 1, __uint_as_float(raw[q].y));
+            put(q * 4 + 2, __uint_as_float(raw[q].z));
+            put(q * 4 + 3, __uint_as_float(raw[q].w));
+          }
         }
       }
     }
@@ -977,6 +771,7 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
 
   // ---- 2. group stage ----
   bool allowed = act;
+  bool redo = false;
   if (a.gstage) {
     float g1 = lm, g2 = l2;
 #pragma unroll
@@ -1001,12 +796,22 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
       const unsigned long long c0 = gc[h], c1 = gc[h + 1];
       rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
     }
-    allowed = act && rank < a.topk_group;
+    const bool keep = rank < a.topk_group;
+    if (!exact) {
+      // the kept groups' lowest score must beat the others' highest by more
+      // than the error of two fast group scores
+      const uint32_t kept_min = seg_min_u32<SEG>(keep ? gsu : 0xFFFFFFFFu);
+      const uint32_t drop_max = seg_max_u32<SEG>(keep ? 0u : gsu);
+      const double gap = (double)s2f(kept_min) - (double)s2f(drop_max);
+      redo = !(gap > 2.0 * epsg);
+    }
+    allowed = act && keep;
     wave_sync_lds();  // every lane has read the composites before step 5 reuses the space
   }
 
   // ---- 3. threshold: k-th largest of the kept lanes' two largest keys ----
-  // At least k keys reach it, so every key of the exact top k does.
+  // At least k keys reach it, so every key of the exact top k does (with fast
+  // keys: every exact top-k key has a fast key >= it - 2 delta).
   const bool two = EPLM >= 2 && (EPL > 0 || epl >= 2);
   const uint32_t u1 = allowed ? f2s(lm) : 0u;
   const uint32_t u2 = (allowed && two) ? f2s(l2) : 0u;
@@ -1041,9 +846,10 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
     }
   }
   const uint32_t T = (NSEG == 1 || seg == 0) ? Ts[0] : Ts[NSEG - 1];
-  const float thr = s2f(T);
+  float thr = s2f(T);
+  if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
   const bool ok = (NSEG == 1 || seg == 0) ? okseg[0] : okseg[NSEG - 1];
-  int status = !act ? TOK_ESCALATE : (ok ? TOK_DONE : TOK_ESCALATE);
+  int status = !act ? TOK_ESCALATE : (!ok ? TOK_ESCALATE : (redo ? TOK_REDO_EXACT : TOK_DONE));
 
   // ---- 4. candidates (keys >= thr), compacted in expert order ----
   // The sign of key - thr is 1 exactly when key < thr (keys are never -0 and a
@@ -1082,10 +888,17 @@ __device__ __forceinline__ int tbl_token(const Args& a, const Lds& L, bool act, 
   float sf = 0.0f;
   unsigned long long mykey = 0ull;  // below every real key
   if (has) {
-    uint32_t h;
-    if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
-    else h = reinterpret_cast<const uint16_t*>(a.logits)[row + ce];
-    sf = sig_lds(sig_off1(h));
+    if constexpr (BF16) {
+      uint32_t h;
+      if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
+      else h = reinterpret_cast<const uint16_t*>(a.logits)[row + ce];
+      sf = sig_lds(sig_off1(h));
+    } else {
+      float x;
+      if constexpr (MODE == LOAD_STAGE) x = reinterpret_cast<const float*>(stage)[ce];
+      else x = reinterpret_cast<const float*>(a.logits)[row + ce];
+      sf = sigmoid_exact(x);
+    }
     mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
   }
   unsigned long long* cc = L.cand_c + w * kWave + seg * SEG;
@@ -1211,18 +1024,10 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         }
       }
       const bool act = tl >= 0;
-      if constexpr (BF16) {
-        const int st = tbl_token<SEG, EPL, MODE>(a, L, act, t0 + tl, tl, cur, bv);
-        if (act && st == TOK_ESCALATE && ls == 0) {
-          const int q = atomicAdd(&L.misc[0], 1);
-          L.esc[q] = tl;
-        }
-        continue;
-      }
-      int st = seg_token<SEG, EPL, BF16, MODE>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
-      if (__ballot(act && st == TOK_REDO_EXACT)) {
+      int st = lean_token<SEG, EPL, BF16, MODE>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
+      if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
         const bool redo = act && st == TOK_REDO_EXACT;
-        const int st2 = seg_token<SEG, EPL, BF16, MODE>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
+        const int st2 = lean_token<SEG, EPL, BF16, MODE>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
         if (redo) st = st2;
       }
       if (act && st == TOK_ESCALATE && ls == 0) {
