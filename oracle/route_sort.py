@@ -196,15 +196,22 @@ class SortMeta:
 
 
 def sort_metadata(ids: np.ndarray, E: int, block: int) -> SortMeta:
-    """Counting sort of token slots s = t*k + j by expert, stable in s."""
+    """Counting sort of token slots s = t*k + j by expert, stable in s.
+
+    A slot whose id lies outside [0, E) is a dropped route: it claims no row
+    and its slot number appears nowhere in sorted_ids (page "gfx1250
+    ordinary-TP route optimization", Dispatch and contracts: negative expert
+    ids claim no slot; ids past E are not counted).  The sentinel stays M*k."""
     ids = np.asarray(ids, dtype=np.int64)
     M, k = ids.shape
     flat = ids.reshape(-1)
-    counts = np.bincount(flat, minlength=E).astype(np.int64)          # phase 1
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int64)   # phase 1
     padded = (counts + block - 1) // block * block
     offsets = np.concatenate([[0], np.cumsum(padded)[:-1]]).astype(np.int64)
     num_post_pad = int(padded.sum())
-    order = np.argsort(flat, kind="stable")                            # phase 2
+    slots = np.flatnonzero(valid)                                      # phase 2
+    order = slots[np.argsort(flat[valid], kind="stable")]
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
     sorted_ids = np.full(num_post_pad, M * k, dtype=np.int64)
     for e in range(E):
@@ -269,9 +276,12 @@ def check_sort_invariants(ids: np.ndarray, sorted_ids: np.ndarray, expert_of_blo
     ids = np.asarray(ids, dtype=np.int64)
     M, k = ids.shape
     sentinel = M * k
-    counts = np.bincount(ids.reshape(-1), minlength=E) if ids.size else np.zeros(E, np.int64)
-    if counts.sum() != M * k:
-        errs.append("histogram does not sum to M*k")
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)  # ids outside [0, E) are dropped routes
+    nvalid = int(valid.sum())
+    counts = np.bincount(flat[valid], minlength=E) if nvalid else np.zeros(E, np.int64)
+    if counts.sum() != nvalid:
+        errs.append("histogram does not sum to the number of routed slots")
     if num_post_pad % block != 0:
         errs.append("num_post_pad not a multiple of block")
     if num_post_pad != int(((counts + block - 1) // block * block).sum()):
@@ -282,8 +292,8 @@ def check_sort_invariants(ids: np.ndarray, sorted_ids: np.ndarray, expert_of_blo
         errs.append("metadata shorter than num_post_pad")
         return errs
     real = rows[rows != sentinel]
-    if real.shape[0] != M * k or not np.array_equal(np.sort(real), np.arange(M * k)):
-        errs.append("real rows are not a bijection onto the token slots")
+    if real.shape[0] != nvalid or not np.array_equal(np.sort(real), np.flatnonzero(valid)):
+        errs.append("real rows are not a bijection onto the routed token slots")
         return errs
     if np.any((rows < 0) | (rows > sentinel)):
         errs.append("row value out of range")
@@ -294,7 +304,6 @@ def check_sort_invariants(ids: np.ndarray, sorted_ids: np.ndarray, expert_of_blo
     nblk = np.bincount(eob, minlength=E) if eob.size else np.zeros(E, np.int64)
     if not np.array_equal(nblk, (counts + block - 1) // block):
         errs.append("blocks per expert differ from ceil(count/block)")
-    flat = ids.reshape(-1)
     blk_of_row = np.arange(num_post_pad) // block
     is_real = rows != sentinel
     if np.any(flat[rows[is_real]] != eob[blk_of_row[is_real]]):

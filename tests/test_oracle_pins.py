@@ -303,6 +303,57 @@ def test_sort_metadata_is_stable_counting_sort():
     assert np.array_equal(real, np.lexsort((np.arange(flat.size), flat)))
 
 
+def _metadata_by_definition_dropping(ids, E, block):
+    """The definition with dropped routes written out: a slot whose id is not
+    in [0, E) takes no row; every other slot goes to its expert's segment in
+    ascending slot order."""
+    M, k = ids.shape
+    flat = [int(v) for v in ids.reshape(-1)]
+    keep = [0 <= e < E for e in flat]
+    counts = [sum(1 for s, e in enumerate(flat) if keep[s] and e == x) for x in range(E)]
+    padded = [-(-c // block) * block for c in counts]
+    off = [sum(padded[:e]) for e in range(E)]
+    rows = [M * k] * sum(padded)
+    fill = [0] * E
+    for s, e in enumerate(flat):
+        if keep[s]:
+            rows[off[e] + fill[e]] = s
+            fill[e] += 1
+    eob = [e for e in range(E) for _ in range(padded[e] // block)]
+    return counts, sum(padded), rows, eob
+
+
+@pytest.mark.parametrize("M,E,k,block", [(1, 8, 3, 4), (6, 6, 2, 1), (7, 10, 3, 3), (16, 12, 4, 5),
+                                         (9, 30, 2, 16)])
+def test_sort_metadata_drops_ids_outside_range(M, E, k, block):
+    """Dropped routes (negative ids, ids >= E) claim no row and no slot; rows
+    may also repeat an expert.  Checked against the definition by brute force."""
+    rng = np.random.default_rng(M + 31 * E + k)
+    for trial in range(6):
+        ids = rng.integers(-3, E + 3, size=(M, k))
+        if trial == 0:
+            ids[:] = -1                      # every route dropped
+        meta = orc.sort_metadata(ids, E, block)
+        counts, total, rows, eob = _metadata_by_definition_dropping(ids, E, block)
+        assert list(meta.counts) == counts
+        assert meta.num_post_pad == total
+        assert list(meta.sorted_ids) == rows
+        assert list(meta.expert_of_block) == eob
+        assert orc.check_sort_invariants(ids, meta.sorted_ids, meta.expert_of_block,
+                                         meta.num_post_pad, E, block) == []
+    ids = np.full((M, k), -1)
+    assert orc.sort_metadata(ids, E, block).num_post_pad == 0
+
+
+def test_checker_rejects_rows_for_dropped_slots():
+    ids = np.array([[0, -1], [1, 5]])  # E = 3: slots 1 and 3 are dropped
+    meta = orc.sort_metadata(ids, 3, 2)
+    assert orc.check_sort_invariants(ids, meta.sorted_ids, meta.expert_of_block, meta.num_post_pad, 3, 2) == []
+    bad = meta.sorted_ids.copy()
+    bad[1] = 1  # the padding row of expert 0 now claims the dropped slot 1
+    assert orc.check_sort_invariants(ids, bad, meta.expert_of_block, meta.num_post_pad, 3, 2) != []
+
+
 # ---------------------------------------------------------------------------
 # The checkers must trip on corrupted metadata (planted mistakes).
 # ---------------------------------------------------------------------------
