@@ -33,6 +33,7 @@ EXPORTED = [
     "moe_route_sort",
     "moe_route_sort_ex",
     "moe_route_sort_profiled",
+    "moe_sort_from_ids",
     "moe_route_sort_max_rows",
     "moe_route_sort_max_blocks",
     "moe_route_sort_workspace_bytes",
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_ex.restype = i32
     L.moe_route_sort_profiled.argtypes = common + [ctypes.c_uint, vp, vp, vp]
     L.moe_route_sort_profiled.restype = i32
+    L.moe_sort_from_ids.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_sort_from_ids.restype = i32
     for name in ("moe_route_sort_max_rows", "moe_route_sort_max_blocks"):
         getattr(L, name).argtypes = [i32, i32, i32, i32]
         getattr(L, name).restype = ctypes.c_int64
@@ -237,3 +240,46 @@ def sigmoid_table_probe(bits):
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return o1, o2
+
+
+class SortOutput(NamedTuple):
+    sorted_ids: "torch.Tensor"       # [max_rows] int32; [0, num_post_pad) defined
+    expert_of_block: "torch.Tensor"  # [max_blocks] int32
+    num_post_pad: "torch.Tensor"     # [1] int32 (device)
+
+
+def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, workspace=None,
+                  stream=None) -> SortOutput:
+    """The two sort phases from caller-given expert ids ([M, k] int32 GPU
+    tensor); ids outside [0, E) are dropped routes."""
+    import torch
+    if not (isinstance(ids, torch.Tensor) and ids.is_cuda and ids.dtype == torch.int32 and ids.dim() == 2
+            and ids.is_contiguous()):
+        raise ValueError("ids must be a contiguous int32 [M, k] GPU tensor")
+    M, k = ids.shape
+    dev = ids.device
+    rows = max_rows(M, E, k, block)
+    blocks = max_blocks(M, E, k, block)
+    if rows < 0:
+        raise ValueError("invalid sizes or row capacity overflow")
+    if out is None:
+        out = SortOutput(torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
+                         torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
+                         torch.empty((1,), dtype=torch.int32, device=dev))
+    elif (out.sorted_ids.numel() < rows or out.expert_of_block.numel() < blocks or
+          out.sorted_ids.dtype != torch.int32 or out.expert_of_block.dtype != torch.int32 or
+          out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
+        raise ValueError("out buffers too small or of the wrong dtype")
+    nbytes = workspace_bytes(M, E, k, block)
+    if workspace is None:
+        workspace = _workspace(dev, nbytes) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
+                                     out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), ws_ptr,
+                                     ws_len, stream.cuda_stream))
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return out

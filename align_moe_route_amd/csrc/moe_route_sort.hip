@@ -98,6 +98,7 @@ struct Args {
   int32_t* ws_hist;  // [nwg][E] per-workgroup counts, then exclusive column prefixes
   int32_t* ws_slot;  // [M*k] expert | (rank inside the workgroup << 16)
   int32_t* stats;
+  const int32_t* in_ids;  // sort-only entry: caller's expert ids [M, k]
 };
 
 // ----------------------------------------------------------------------------
@@ -1259,10 +1260,154 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
     const int q = tid + j * kWG;
-    if (q < ns) {
+    if (q < ns && rv[j] >= 0) {  // a negative record is a dropped route (sort-only entry)
       const int e = rv[j] & 0xFFFF;
       a.sorted_ids[L.off[e] + L.cpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Sort-only entry: the two sort phases from expert ids given by the caller.
+// An id outside [0, E) is a dropped route: it claims no row (page "gfx1250
+// ordinary-TP route optimization", Dispatch and contracts).
+// ----------------------------------------------------------------------------
+struct IdsLds {
+  unsigned long long* bits;  // [E] bit tl: token tl of the workgroup routes to e
+  int* cnt;                  // [E] routes of the workgroup per expert
+  int* rec;                  // [tw*k] expert | rank << 16, or -1 for a dropped route
+  int* off;                  // [E] expert offsets (single-workgroup kernel)
+  int* misc;
+  int* scan;
+};
+__host__ __device__ inline size_t ids_lds_bytes(int E, int tw, int k, size_t* o_cnt, size_t* o_rec, size_t* o_off,
+                                                size_t* o_misc, size_t* o_scan) {
+  size_t o = 0;
+  auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
+  take((size_t)E * 8);
+  *o_cnt = take((size_t)E * 4);
+  *o_rec = take((size_t)tw * k * 4);
+  *o_off = take((size_t)E * 4);
+  *o_misc = take(16 * 4);
+  *o_scan = take((size_t)kNW * 4);
+  return o;
+}
+__device__ inline IdsLds ids_carve(const Args& a) {
+  size_t oc, orc, oo, om, osc;
+  ids_lds_bytes(a.E, a.tw, a.k, &oc, &orc, &oo, &om, &osc);
+  IdsLds L;
+  L.bits = reinterpret_cast<unsigned long long*>(g_lds);
+  L.cnt = reinterpret_cast<int*>(g_lds + oc);
+  L.rec = reinterpret_cast<int*>(g_lds + orc);
+  L.off = reinterpret_cast<int*>(g_lds + oo);
+  L.misc = reinterpret_cast<int*>(g_lds + om);
+  L.scan = reinterpret_cast<int*>(g_lds + osc);
+  return L;
+}
+
+// Counts and stable ranks of the slots of tokens [t0, t0+nt).  With distinct
+// ids in every row the rank of slot (tl, j) is the number of earlier tokens of
+// the workgroup routed to the same expert (a popcount of the bitset); when a
+// row repeats an expert, one thread ranks the slots in slot order instead.
+__device__ void ids_local(const Args& a, const IdsLds& L, int t0, int nt) {
+  const int tid = threadIdx.x;
+  const int ns = nt * a.k;
+  const int32_t* src = a.in_ids + (size_t)t0 * a.k;
+  for (int e = tid; e < a.E; e += kWG) L.bits[e] = 0ull;
+  if (tid == 0) L.misc[0] = 0;
+  int iv[kRecPerThread];
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j) {
+    const int q = tid + j * kWG;
+    iv[j] = q < ns ? src[q] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j) {
+    const int q = tid + j * kWG;
+    const int e = iv[j];
+    if (q < ns && e >= 0 && e < a.E) {
+      const unsigned long long bit = 1ull << (q / a.k);
+      if (atomicOr(&L.bits[e], bit) & bit) L.misc[0] = 1;  // this token already routes to e
+    }
+  }
+  __syncthreads();
+  if (L.misc[0] == 0) {
+    for (int e = tid; e < a.E; e += kWG) L.cnt[e] = __popcll(L.bits[e]);
+#pragma unroll
+    for (int j = 0; j < kRecPerThread; ++j) {
+      const int q = tid + j * kWG;
+      const int e = iv[j];
+      if (q < ns) {
+        const int tl = q / a.k;
+        L.rec[q] = (e >= 0 && e < a.E) ? (e | (__popcll(L.bits[e] & ((1ull << tl) - 1ull)) << 16)) : -1;
+      }
+    }
+  } else {
+    for (int e = tid; e < a.E; e += kWG) L.cnt[e] = 0;
+    __syncthreads();
+    if (tid == 0) {
+      for (int q = 0; q < ns; ++q) {
+        const int e = src[q];
+        L.rec[q] = (e >= 0 && e < a.E) ? (e | (L.cnt[e]++ << 16)) : -1;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Multi-workgroup path, launch 1: per-workgroup histogram row and slot records.
+__global__ __launch_bounds__(kWG) void k_ids_hist(Args a) {
+  const IdsLds L = ids_carve(a);
+  const int w = blockIdx.x;
+  const int t0 = w * a.tw;
+  const int nt = min(a.tw, a.M - t0);
+  ids_local(a, L, t0, nt);
+  for (int e = threadIdx.x; e < a.E; e += kWG) a.ws_hist[(size_t)w * a.E + e] = L.cnt[e];
+  const int ns = nt * a.k;
+  int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
+  for (int q = threadIdx.x; q < ns; q += kWG) rec[q] = L.rec[q];
+}
+
+// M <= 64: the whole sort in one workgroup.
+__global__ __launch_bounds__(kWG) void k_ids_small(Args a) {
+  const IdsLds L = ids_carve(a);
+  const int tid = threadIdx.x;
+  ids_local(a, L, 0, a.M);
+  const int ept = (a.E + kWG - 1) / kWG;
+  const int e0 = tid * ept;
+  int local = 0;
+  for (int i = 0; i < ept; ++i)
+    if (e0 + i < a.E) local += pad_block(L.cnt[e0 + i], a);
+  int pre = 0;
+  {  // exclusive scan of the padded counts (wave scan, then across waves)
+    const int w = tid >> 6;
+    const int x = wave_incl_scan(local);
+    if (lane_id() == kWave - 1) L.scan[w] = x;
+    __syncthreads();
+    for (int q = 0; q < w; ++q) pre += L.scan[q];
+    pre += x - local;
+  }
+  for (int i = 0; i < ept; ++i) {
+    const int e = e0 + i;
+    if (e < a.E) {
+      L.off[e] = pre;
+      pre += pad_block(L.cnt[e], a);
+    }
+  }
+  if (tid == kWG - 1) *a.npp = pre;
+  __syncthreads();
+  const int sentinel = a.M * a.k;
+  for (int e = tid; e < a.E; e += kWG) {
+    const int c = L.cnt[e];
+    const int p = pad_block(c, a);
+    const int o = L.off[e];
+    for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
+    for (int b = div_block(o, a); b < div_block(o + p, a); ++b) a.eob[b] = e;
+  }
+  for (int q = tid; q < sentinel; q += kWG) {
+    const int r = L.rec[q];
+    if (r >= 0) a.sorted_ids[L.off[r & 0xFFFF] + (r >> 16)] = q;
   }
 }
 
@@ -1368,6 +1513,7 @@ bool seg32_epl(int epl) {
       case 14: return fix_##KER<64, 14, BF16>();                                                   \
       case 16: return fix_##KER<64, 16, BF16>();                                                   \
       case 32: return fix_##KER<64, 32, BF16>();                                                   \
+      case 64: return fix_##KER<64, 64, BF16>();                                                   \
       default: return mode == LOAD_VEC ? KER<64, 0, BF16, LOAD_VEC> : KER<64, 0, BF16, LOAD_STAGE>; \
     }                                                                                              \
   }                                                                                                \
@@ -1654,6 +1800,66 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
   return moe_route_sort_ex(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
                            sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
                            workspace_bytes, stream, 0u, nullptr);
+}
+
+int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_t* sorted_ids,
+                      int32_t* expert_of_block, int32_t* num_post_pad, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!valid_sizes(M, E, k, block)) return MRS_ERR_INVALID_ARG;
+  if ((int64_t)M * k > INT32_MAX || max_rows_of(M, E, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if (num_post_pad == nullptr) return MRS_ERR_NULL_POINTER;
+  if (!aligned(num_post_pad, 4)) return MRS_ERR_MISALIGNED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M == 0) {
+    void* params[] = {&num_post_pad};
+    return launch(reinterpret_cast<const void*>(k_zero_npp), 1, 1, 0, st, params, nullptr);
+  }
+  if (!ids || !sorted_ids || !expert_of_block) return MRS_ERR_NULL_POINTER;
+  if (!aligned(ids, 4) || !aligned(sorted_ids, 4) || !aligned(expert_of_block, 4)) return MRS_ERR_MISALIGNED;
+  Args a{};
+  a.M = M;
+  a.E = E;
+  a.k = k;
+  a.block = block;
+  {
+    uint32_t l = 0;
+    while ((1ull << l) < (unsigned long long)block) ++l;
+    a.blk_sh = 31 + l;
+    a.blk_mul = ((1ull << (31 + l)) + (unsigned long long)block - 1) / (unsigned long long)block;
+  }
+  a.in_ids = ids;
+  a.sorted_ids = sorted_ids;
+  a.eob = expert_of_block;
+  a.npp = num_post_pad;
+  size_t oc, orc, oo, om, osc;
+  void* p_one[] = {&a};
+  if (M <= kTwMax) {
+    a.tw = M;
+    a.nwg = 1;
+    const size_t lds = ids_lds_bytes(E, M, k, &oc, &orc, &oo, &om, &osc);
+    if (lds > kLdsLimit) return MRS_ERR_INVALID_ARG;
+    return launch(reinterpret_cast<const void*>(k_ids_small), 1, kWG, lds, st, p_one, nullptr);
+  }
+  a.tw = choose_tw(M);
+  a.nwg = (M + a.tw - 1) / a.tw;
+  const size_t need = workspace_of(M, E, k);
+  if (workspace == nullptr || workspace_bytes < need) return MRS_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MRS_ERR_MISALIGNED;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace) + kWsHeader;
+  a.ws_tot = reinterpret_cast<int32_t*>(ws);
+  a.ws_pad = a.ws_tot + E;
+  ws += align16((size_t)2 * E * 4);
+  a.ws_hist = reinterpret_cast<int32_t*>(ws);
+  ws += align16((size_t)a.nwg * E * 4);
+  a.ws_slot = reinterpret_cast<int32_t*>(ws);
+  const size_t lds_h = ids_lds_bytes(E, a.tw, k, &oc, &orc, &oo, &om, &osc);
+  const size_t lds_sct = lds_plan(KIND_SCATTER, E, 1, 0, 0, a.tw, k, 0).total;
+  if (lds_h > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
+  int rc = launch(reinterpret_cast<const void*>(k_ids_hist), a.nwg, kWG, lds_h, st, p_one, nullptr);
+  if (rc == MRS_OK)
+    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kWave - 1) / kWave, kWG, 0, st, p_one, nullptr);
+  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, nullptr);
+  return rc;
 }
 
 int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* out_single,

@@ -138,6 +138,31 @@ int moe_route_sort_profiled(const void* logits, const float* bias, int M, int E,
                             int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
                             unsigned flags, int32_t* stats, void* const* events, int* n_launches);
 
+/*
+ * moe_sort_from_ids -- the two sort phases alone, from expert ids chosen
+ * elsewhere (page "gfx1250 ordinary-TP route optimization", Summary and
+ * Dispatch and contracts: route rows built from selected ids with workgroup
+ * histograms).
+ *
+ *   ids             [M, k] int32 device array, 4-byte aligned.  Slot t*k + j
+ *                   routes to expert ids[t*k + j]; an id outside [0, E) is a
+ *                   dropped route: it claims no row and its slot number does
+ *                   not appear in sorted_ids.  A row may repeat an expert
+ *                   (each slot then takes its own row; such workgroups are
+ *                   ranked by a slower serial pass).
+ *   M, E, k, block  as for moe_route_sort (k <= 64, E <= 4096).
+ *   sorted_ids, expert_of_block, num_post_pad
+ *                   the metadata of moe_route_sort with counts over the routed
+ *                   slots only (same capacities, same sentinel M*k).
+ *   workspace       as for moe_route_sort, same size
+ *                   (moe_route_sort_workspace_bytes).
+ * Asynchronous on `stream`; never allocates or waits.  Returns MRS_OK or a
+ * negative MRS_ERR_* code, detected before any launch.
+ */
+int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_t* sorted_ids,
+                      int32_t* expert_of_block, int32_t* num_post_pad, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Capacity of sorted_ids: M*k + min(E, M*k)*(block-1), or -1 when the
  * arguments are invalid or the result does not fit int32. */
 int64_t moe_route_sort_max_rows(int M, int E, int k, int block);

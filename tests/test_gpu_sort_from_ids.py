@@ -1,0 +1,111 @@
+"""GPU parity of the sort-only entry point (moe_sort_from_ids) against the
+oracle's sort metadata: exact counts, stable rows, padding, expert per block,
+dropped routes (ids outside [0, E)), rows that repeat an expert, and agreement
+with the full route-sort call on its own ids."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import route_sort as orc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+amr = pytest.importorskip("align_moe_route_amd")
+
+
+def distinct_rows(rng, M, E, k, skew=0.0):
+    """k distinct experts per row; with skew > 0 popular experts are likelier."""
+    p = None
+    if skew > 0:
+        w = 1.0 / np.arange(1, E + 1) ** skew
+        p = w[rng.permutation(E)] / w.sum()
+    return np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(M)]).astype(np.int32)
+
+
+def run_and_check(ids, E, block):
+    M, k = ids.shape
+    print(f"[gpu] sort_from_ids M={M} E={E} k={k} block={block} dropped={int(((ids < 0) | (ids >= E)).sum())}",
+          flush=True)
+    out = amr.sort_from_ids(torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda(), E, block)
+    torch.cuda.synchronize()
+    npp = int(out.num_post_pad.item())
+    rows = out.sorted_ids[:npp].cpu().numpy()
+    eob = out.expert_of_block[:npp // block].cpu().numpy()
+    ref = orc.sort_metadata(ids, E, block)
+    assert npp == ref.num_post_pad
+    assert np.array_equal(rows, ref.sorted_ids)
+    assert np.array_equal(eob, ref.expert_of_block)
+    assert orc.check_sort_invariants(ids, rows, eob, npp, E, block) == []
+    return out
+
+
+@pytest.mark.parametrize("M,E,k,block,skew", [
+    (1, 896, 16, 32, 0.0), (4, 64, 4, 16, 0.0), (64, 896, 16, 128, 1.1), (65, 128, 8, 7, 0.0),
+    (300, 4096, 16, 128, 0.5), (1000, 129, 5, 1, 0.0), (2517, 896, 16, 128, 1.1),
+    (8192, 896, 16, 128, 1.1), (5000, 1, 1, 3, 0.0)])
+def test_distinct_ids(M, E, k, block, skew):
+    rng = np.random.default_rng(M + E)
+    run_and_check(distinct_rows(rng, M, E, k, skew), E, block)
+
+
+@pytest.mark.parametrize("M,E,k,block", [(3, 64, 8, 16), (64, 896, 16, 32), (700, 896, 16, 64),
+                                         (9000, 512, 8, 128)])
+def test_dropped_ids(M, E, k, block):
+    rng = np.random.default_rng(7 * M + E)
+    ids = distinct_rows(rng, M, E, k)
+    mask = rng.random(ids.shape) < 0.2
+    ids[mask] = rng.choice(np.array([-1, -7, E, E + 100, 2 ** 31 - 1, -2 ** 31]), size=int(mask.sum()))
+    run_and_check(ids, E, block)
+
+
+@pytest.mark.parametrize("M", [5, 600])
+def test_all_dropped(M):
+    ids = np.full((M, 4), -1, dtype=np.int32)
+    out = run_and_check(ids, 32, 8)
+    assert int(out.num_post_pad.item()) == 0
+
+
+@pytest.mark.parametrize("M,E,k,block", [(10, 16, 6, 4), (200, 24, 8, 16)])
+def test_rows_repeating_an_expert(M, E, k, block):
+    """Each slot takes its own row even when a row names an expert twice."""
+    rng = np.random.default_rng(M * k)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]
+    run_and_check(ids, E, block)
+
+
+def test_matches_full_route_sort():
+    cfg = workloads.custom(3000, 896, 16, 8, 4, 128, "bf16", "log_zipf", seed=12)
+    inp = workloads.make_inputs(cfg)
+    x = torch.from_numpy(inp.logits_storage.view(np.int16)).view(torch.bfloat16).cuda()
+    b = torch.from_numpy(inp.bias).cuda()
+    full = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    srt = amr.sort_from_ids(full.ids, cfg.E, cfg.block)
+    torch.cuda.synchronize()
+    npp = int(full.num_post_pad.item())
+    assert int(srt.num_post_pad.item()) == npp
+    assert torch.equal(srt.sorted_ids[:npp], full.sorted_ids[:npp])
+    assert torch.equal(srt.expert_of_block[:npp // cfg.block], full.expert_of_block[:npp // cfg.block])
+
+
+def test_poisoned_tails_untouched():
+    rng = np.random.default_rng(5)
+    M, E, k, block = 500, 896, 16, 64
+    ids = distinct_rows(rng, M, E, k, 1.1)
+    rows, blocks = amr.max_rows(M, E, k, block), amr.max_blocks(M, E, k, block)
+    poison = -99
+    out = amr.SortOutput(torch.full((rows + 32,), poison, dtype=torch.int32, device="cuda"),
+                         torch.full((blocks + 32,), poison, dtype=torch.int32, device="cuda"),
+                         torch.full((1,), poison, dtype=torch.int32, device="cuda"))
+    g = torch.from_numpy(ids).cuda()
+    g0 = g.clone()
+    amr.sort_from_ids(g, E, block, out=out)
+    torch.cuda.synchronize()
+    npp = int(out.num_post_pad.item())
+    ref = orc.sort_metadata(ids, E, block)
+    assert npp == ref.num_post_pad
+    assert np.array_equal(out.sorted_ids[:npp].cpu().numpy(), ref.sorted_ids)
+    assert torch.all(out.sorted_ids[npp:] == poison)
+    assert torch.all(out.expert_of_block[npp // block:] == poison)
+    assert torch.equal(g, g0)

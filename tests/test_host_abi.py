@@ -21,7 +21,7 @@ Q = 0x20000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_route_sort\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_(?:route_)?sort\w*)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -141,3 +141,30 @@ def test_sigmoid_table_probe_validation():
     assert L.moe_route_sort_sigmoid_table_probe(P, 0, P, P, None) == amr.MRS_OK
     assert L.moe_route_sort_sigmoid_table_probe(None, 5, P, P, None) == amr.MRS_ERR_NULL_POINTER
     assert L.moe_route_sort_sigmoid_table_probe(P + 1, 5, P, P, None) == amr.MRS_ERR_MISALIGNED
+
+
+def ids_call(**kw):
+    """moe_sort_from_ids with fake aligned pointers (validation only)."""
+    L = amr.lib()
+    d = dict(ids=P, M=4, E=64, k=4, block=16, rows=P, eob=P, npp=P, ws=None, ws_bytes=0)
+    d.update(kw)
+    return L.moe_sort_from_ids(d["ids"], d["M"], d["E"], d["k"], d["block"], d["rows"], d["eob"], d["npp"],
+                               d["ws"], d["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(E=0), dict(E=4097), dict(k=0), dict(k=65), dict(block=0)])
+def test_sort_from_ids_invalid_arguments(kw):
+    assert ids_call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_sort_from_ids_checks():
+    assert ids_call(M=1 << 26, k=64, E=64) == amr.MRS_ERR_OVERFLOW
+    for name in ("ids", "rows", "eob", "npp"):
+        assert ids_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER
+    for name in ("ids", "rows", "eob", "npp"):
+        assert ids_call(**{name: P + 2}) == amr.MRS_ERR_MISALIGNED
+    need = amr.workspace_bytes(8192, 896, 16, 128)
+    assert ids_call(M=8192, E=896, k=16, block=128) == amr.MRS_ERR_WORKSPACE
+    assert ids_call(M=8192, E=896, k=16, block=128, ws=Q, ws_bytes=need - 4) == amr.MRS_ERR_WORKSPACE
+    assert ids_call(M=8192, E=896, k=16, block=128, ws=Q + 4, ws_bytes=need + 64) == amr.MRS_ERR_MISALIGNED
+    assert ids_call(M=0, npp=None) == amr.MRS_ERR_NULL_POINTER
