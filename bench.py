@@ -141,6 +141,37 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     return r
 
 
+def time_sort_from_ids(cfg, steps, torch, amr):
+    """The sort-only entry point on the ids the full path chose for this
+    workload (same skew), timed like the main loop (graph replay)."""
+    inp = workloads.make_inputs(cfg)
+    x0, b = to_gpu(inp, torch)
+    ids = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block).ids
+    out = amr.sort_from_ids(ids, cfg.E, cfg.block)
+    torch.cuda.synchronize()
+    G = graph_size(steps)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(G):
+            amr.sort_from_ids(ids, cfg.E, cfg.block, out=out)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps // G):
+            graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    npp = int(out.num_post_pad.item())
+    nbytes = 4 * cfg.M * cfg.k + 4 * npp + 4 * (npp // cfg.block) + 4
+    return dict(us_per_call=round(ms * 1e3, 3), routes_per_s=cfg.M * cfg.k / (ms * 1e-3),
+                algorithmic_gbps=round(nbytes / (ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
+
+
 def traffic_record(kernel, workload):
     """HBM traffic per launch measured with rocprofv3 PMC counters and stored
     under profiles/, used only while the kernel source still has the hash the
@@ -236,6 +267,12 @@ def main():
                                frac_hbm_peak=round(e["gbps"] / HBM_PEAK_GBPS, 4))
             log(f"[bench] {name}: {e['ms']*1e3:.2f} us/call, {e['routes_per_s']:.3e} routes/s, "
                 f"{e['gbps']:.1f} GB/s")
+
+    if not args.no_extra:
+        so = time_sort_from_ids(cfg, max(20, args.steps // 4), torch, amr)
+        extra["sort_from_ids_" + cfg.name] = so
+        log(f"[bench] sort_from_ids on {cfg.name} ids: {so['us_per_call']:.2f} us/call, "
+            f"{so['routes_per_s']:.3e} routes/s")
 
     cpu = None
     if not args.no_cpu_baseline:
