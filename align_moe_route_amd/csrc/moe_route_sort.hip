@@ -971,7 +971,11 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
                                          (__attribute__((address_space(3))) void*)(dst + j * kWG * 16 + wbase), 16,
                                          0, 0);
   }
-  if (!a.rows_first && a.fast && MODE == LOAD_STAGE) {
+  // With one round per wave, the second half of the waves requests its rows
+  // only after the shared data has arrived: the first half's rows then land
+  // sooner and their compute overlaps the second half's transfer.
+  const bool late = !a.rows_first && a.nbuf == 1 && w >= kNW / 2;
+  if (!a.rows_first && !late && a.fast && MODE == LOAD_STAGE) {
     const int tl = tok_of(0);
     stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
   }
@@ -984,10 +988,14 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     // loads complete in order: with R row copies issued after the shared
     // data, vmcnt <= R means the table and bias copies of this wave are done
     constexpr int R = EPL > 0 ? row_dma_count<SEG, EPL, BF16 ? 2 : 4>() : 0;
-    if (!a.rows_first && a.fast && MODE == LOAD_STAGE && R > 0) wait_vmem_upto<R>();
+    if (!a.rows_first && !late && a.fast && MODE == LOAD_STAGE && R > 0) wait_vmem_upto<R>();
     else wait_vmem_all();
   }
   __syncthreads();
+  if (late && a.fast && MODE == LOAD_STAGE) {
+    const int tl = tok_of(0);
+    stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
+  }
   if (a.fast) {
     const int epl = EPL > 0 ? EPL : a.epl;
     const int e0 = ls * epl;
