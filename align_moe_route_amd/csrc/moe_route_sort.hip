@@ -1257,13 +1257,15 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   const int total = L.misc[1];
   if (w == 0 && tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
-  for (int e = es0; e < es1; ++e) {
+  // one wave per expert of this block's share: padding rows, expert_of_block
+  const int lane = lane_id();
+  for (int e = es0 + (tid >> 6); e < es1; e += kNW) {
     const int c = cnt[e - es0];
     const int o = L.off[e];
     const int p = (e + 1 < a.E ? L.off[e + 1] : total) - o;
-    for (int r = c + tid; r < p; r += kWG) a.sorted_ids[o + r] = sentinel;
+    for (int r = c + lane; r < p; r += kWave) a.sorted_ids[o + r] = sentinel;
     const int b0 = div_block(o, a), nb = div_block(p, a);
-    for (int b = tid; b < nb; b += kWG) a.eob[b0 + b] = e;
+    for (int b = lane; b < nb; b += kWave) a.eob[b0 + b] = e;
   }
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
