@@ -6,33 +6,42 @@
 // block-padded dispatch metadata for a grouped GEMM.  Exact definitions of
 // every output are in include/moe_route_sort.h.
 //
-// Selection (one wave64 per token; lane l owns experts [l*epl, (l+1)*epl))
-//   1. keys A = fast_sigmoid(x) + b for all experts (|A - exact key| <= delta)
-//      and each lane's top two keys;
-//   2. group stage: top-2 merged across the lanes of a group with DPP, group
-//      score, rank of every group by (score desc, index asc); the boundary is
-//      accepted only if the topk_group-th and next scores differ by more than
-//      the error of the fast scores, else the token is redone with exact keys;
-//   3. threshold tau0 = k-th largest lane maximum among the kept lanes (at
-//      least k keys reach it), by a short bisection from the highest differing
-//      bit; every exact top-k expert has A >= tau0 - 2*delta;
-//   4. the (typically ~20, at most 64) candidates above that line are
-//      compacted in expert order; each candidate lane computes its correctly
-//      rounded sigmoid and exact key; exact ranks by (key desc, index asc)
-//      pick the k experts, so the result is exact without any tie exemption;
+// Workgroups of 1024 threads (16 waves) take tw = ceil(M / 256) consecutive
+// tokens each (one workgroup per compute unit at the 8192-token shape); the
+// rows are copied into LDS with global_load_lds (wave by wave, so a wave's
+// compute overlaps the others' copies) or read as 16-byte vectors.
+//
+// Selection, one token per wave segment of 32 or 64 lanes; lane l owns
+// experts [l*epl, (l+1)*epl):
+//   1. keys = sigmoid(x) + b and each lane's two largest keys.  BF16 logits
+//      look their sigmoid up in an LDS table that is correctly rounded for
+//      every BF16 value, so the keys are exact.  FP32 logits use sigmoid_fast
+//      (|key error| <= delta) to find candidates only;
+//   2. group stage: each group's top two merged across its lanes with DPP,
+//      group score, rank of every group by (score desc, index asc) by counting
+//      in LDS.  With fast keys the kept set is accepted only if it beats the
+//      dropped groups by more than the fast scores' error, else the token is
+//      redone in the same wave with correctly rounded keys;
+//   3. threshold: a lower bound of the k-th largest of the kept lanes' top-two
+//      keys (at least k keys reach it), by ballot-count bisection over the
+//      highest differing bits; with fast keys it is lowered by 2*delta;
+//   4. the candidates above it (about 16-20) are compacted in expert order;
+//      their exact keys are ranked by (key desc, index asc), which picks the k
+//      experts exactly, with no tie exemption;
 //   5. weights from the same exact sigmoid values, normalised in float64.
-//   A token with more than 64 candidates (heavy exact ties) and every token of
-//   a shape outside this layout is decided by the whole workgroup from exact
-//   keys held in LDS.
+//   A token with more candidates than lanes (heavy exact ties) and every token
+//   of a shape outside this layout is decided by the whole workgroup from
+//   exact keys held in LDS.
 // Histogram and ranks: per-workgroup LDS bitsets, bit tl of word e set when
 //   token tl of the workgroup picked expert e.  Popcount = the workgroup's
 //   count for e (no global atomic per route; compare the workgroup histograms
 //   of the page "gfx1250 ordinary-TP route optimization", Summary); popcount
 //   of the bits below tl = the slot's stable rank inside the workgroup.
 // Large M: three launches -- select (+ histogram row, slot records), column
-//   scan of the histograms in workgroup order, scatter.  On MI355X a device-
-//   wide barrier inside one launch costs tens of microseconds (agent-scope
-//   release/acquire across the eight XCDs), far more than a kernel boundary.
+//   scan of the histograms in workgroup order, scatter.  Exchanging those rows
+//   between workgroups inside one launch needs agent-scope (cross-XCD) memory
+//   round trips of about 2 us each on MI355X; the two kernel boundaries cost
+//   less than the two device-wide waits that would replace them.
 // M <= 64: everything in one workgroup and one launch.
 
 #include <hip/hip_ext.h>
