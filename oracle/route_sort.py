@@ -16,7 +16,7 @@ route optimization" (Capacity and dispatch; Dispatch and contracts; Tests and
 compatibility) supplies the route-row invariants used by the checkers below:
 exact counts, a row-slot bijection and per-expert ownership.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   * scoring is the logistic sigmoid, s = RN32(1 / (1 + exp(-x))), correctly
     rounded to FP32;
   * the correction bias is added to the score used for choosing,
