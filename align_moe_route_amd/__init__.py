@@ -40,6 +40,8 @@ EXPORTED = [
     "moe_route_sort_strerror",
     "moe_route_sort_sigmoid_probe",
     "moe_route_sort_sigmoid_table_probe",
+    "moe_grouped_gemm1",
+    "moe_grouped_gemm1_profiled",
 ]
 
 _lib = None
@@ -81,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_sigmoid_probe.restype = i32
     L.moe_route_sort_sigmoid_table_probe.argtypes = [vp, i32, vp, vp, vp]
     L.moe_route_sort_sigmoid_table_probe.restype = i32
+    L.moe_grouped_gemm1.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    L.moe_grouped_gemm1.restype = i32
+    L.moe_grouped_gemm1_profiled.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.moe_grouped_gemm1_profiled.restype = i32
     _lib = L
     return L
 
@@ -280,6 +286,58 @@ def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, 
     rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
                                      out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), ws_ptr,
                                      ws_len, stream.cuda_stream))
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return out
+
+
+def grouped_gemm1(x, w, sorted_ids, expert_of_block, num_post_pad, k: int, block: int, *,
+                  out=None, stream=None, events=None):
+    """First grouped GEMM of the MoE over the route-sort metadata
+    (include/moe_gemm1.h): y[r] = x[sorted_ids[r] // k] . W[expert_of_block[r // block]]^T
+    for sorted rows below num_post_pad, zeros for padding rows.
+
+    x: [M, K] bfloat16, w: [E, N, K] bfloat16, metadata as returned by
+    route_sort / sort_from_ids.  Returns y, [max_rows, N] bfloat16 (rows at
+    or past num_post_pad are left as they were).  `events` = (start, stop)
+    torch.cuda.Event pair stamped by the kernel's own launch."""
+    import torch
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2
+            and x.is_contiguous()):
+        raise ValueError("x must be a contiguous bfloat16 [M, K] GPU tensor")
+    if not (isinstance(w, torch.Tensor) and w.device == x.device and w.dtype == torch.bfloat16 and w.dim() == 3
+            and w.is_contiguous()):
+        raise ValueError("w must be a contiguous bfloat16 [E, N, K] tensor on x's device")
+    M, K = x.shape
+    E, N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    rows = max_rows(M, E, k, block)
+    blocks = max_blocks(M, E, k, block)
+    if rows < 0:
+        raise ValueError("invalid sizes or row capacity overflow")
+    for t, n, name in ((sorted_ids, rows, "sorted_ids"), (expert_of_block, blocks, "expert_of_block"),
+                       (num_post_pad, 1, "num_post_pad")):
+        if not (isinstance(t, torch.Tensor) and t.device == x.device and t.dtype == torch.int32
+                and t.is_contiguous() and t.numel() >= n):
+            raise ValueError(f"{name} must be a contiguous int32 tensor of at least {n} entries on x's device")
+    if out is None:
+        out = torch.empty((max(rows, 1), N), dtype=torch.bfloat16, device=x.device)
+    elif not (out.device == x.device and out.dtype == torch.bfloat16 and out.is_contiguous()
+              and out.dim() == 2 and out.shape[1] == N and out.shape[0] >= rows):
+        raise ValueError("out must be a contiguous bfloat16 [max_rows, N] tensor on x's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    args = (x.data_ptr(), w.data_ptr(), sorted_ids.data_ptr(), expert_of_block.data_ptr(),
+            num_post_pad.data_ptr(), M, k, E, K, N, block, out.data_ptr(), stream.cuda_stream)
+    if events is not None:
+        ev0, ev1 = events
+        for ev in (ev0, ev1):
+            if not ev.cuda_event:
+                ev.record(stream)  # torch creates the HIP event on its first record
+        rc = int(lib().moe_grouped_gemm1_profiled(*args, ev0.cuda_event, ev1.cuda_event))
+    else:
+        rc = int(lib().moe_grouped_gemm1(*args))
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return out

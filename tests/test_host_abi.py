@@ -11,7 +11,8 @@ import pytest
 import align_moe_route_amd as amr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_route_sort.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 # aligned fake device addresses: never dereferenced, validation fails first
 P = 0x10000
@@ -19,9 +20,11 @@ Q = 0x20000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_(?:route_)?sort\w*)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -168,3 +171,29 @@ def test_sort_from_ids_checks():
     assert ids_call(M=8192, E=896, k=16, block=128, ws=Q, ws_bytes=need - 4) == amr.MRS_ERR_WORKSPACE
     assert ids_call(M=8192, E=896, k=16, block=128, ws=Q + 4, ws_bytes=need + 64) == amr.MRS_ERR_MISALIGNED
     assert ids_call(M=0, npp=None) == amr.MRS_ERR_NULL_POINTER
+
+
+def gemm_call(**kw):
+    L = amr.lib()
+    d = dict(x=P, w=P, sid=Q, eob=Q, npp=Q, M=64, k=8, E=64, K=256, N=256, block=64, y=P)
+    d.update(kw)
+    return L.moe_grouped_gemm1(d["x"], d["w"], d["sid"], d["eob"], d["npp"], d["M"], d["k"], d["E"], d["K"],
+                               d["N"], d["block"], d["y"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(k=0), dict(k=65), dict(E=0), dict(E=4097), dict(K=0),
+                                dict(K=96), dict(N=0), dict(N=192), dict(block=16), dict(block=48)])
+def test_grouped_gemm1_invalid_arguments(kw):
+    assert gemm_call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_grouped_gemm1_checks():
+    for name in ("x", "w", "sid", "eob", "npp", "y"):
+        assert gemm_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER
+    for name in ("x", "w", "y"):
+        assert gemm_call(**{name: P + 8}) == amr.MRS_ERR_MISALIGNED
+    assert gemm_call(M=1 << 26, k=64) == amr.MRS_ERR_OVERFLOW
+    assert gemm_call(M=0) == amr.MRS_OK  # no row can exist: returns before any launch
+    L = amr.lib()
+    assert L.moe_grouped_gemm1_profiled(P, P, Q, Q, Q, 64, 8, 64, 256, 256, 64, P, None, None, None) == \
+        amr.MRS_ERR_NULL_POINTER
