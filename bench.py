@@ -172,6 +172,53 @@ def time_sort_from_ids(cfg, steps, torch, amr):
                 algorithmic_gbps=round(nbytes / (ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
 
 
+GEMM_K, GEMM_N = 3584, 768     # Kimi-K3 TP8 routed MoE: hidden 3584, 2 x intermediate 384
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+
+
+def time_gemm1(cfg, steps, torch, amr):
+    """The grouped GEMM1 consumer on this workload's metadata (device-resident,
+    straight from the route-sort call), random BF16 hidden states and expert
+    weights of the Kimi-K3 TP8 shape; each launch timed by its own start/end
+    events."""
+    inp = workloads.make_inputs(cfg)
+    x0, b = to_gpu(inp, torch)
+    meta = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    K, N = GEMM_K, GEMM_N
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((cfg.M, K), generator=g, device="cuda").to(torch.bfloat16)
+    w = torch.empty((cfg.E, N, K), dtype=torch.bfloat16, device="cuda")
+    for e0 in range(0, cfg.E, 64):  # in slices, so the FP32 draw stays small
+        w[e0:e0 + 64] = (torch.randn((min(64, cfg.E - e0), N, K), generator=g, device="cuda")
+                         * K ** -0.5).to(torch.bfloat16)
+    y = amr.grouped_gemm1(x, w, meta.sorted_ids, meta.expert_of_block, meta.num_post_pad, cfg.k, cfg.block)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        amr.grouped_gemm1(x, w, meta.sorted_ids, meta.expert_of_block, meta.num_post_pad, cfg.k, cfg.block,
+                          out=y, events=evs[i])
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(z) for a, z in evs])) * 1e3
+    npp = int(meta.num_post_pad.item())
+    counts = torch.bincount(meta.ids.reshape(-1).long(), minlength=cfg.E)
+    active = int((counts > 0).sum().item())
+    flops = 2.0 * cfg.M * cfg.k * N * K                  # routed rows only
+    padded_flops = 2.0 * npp * N * K                     # what the tiles compute
+    nbytes = active * N * K * 2 + cfg.M * K * 2 + npp * N * 2 + 4 * npp + 4 * (npp // cfg.block) + 4
+    del w
+    torch.cuda.empty_cache()
+    tflops = flops / (us * 1e-6) / 1e12
+    gbps = nbytes / (us * 1e-6) / 1e9
+    t_mfma = padded_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9) * 1e6
+    return dict(kernel="k_gemm1", K=K, N=N, us_per_call=round(us, 2), num_post_pad=npp, active_experts=active,
+                useful_tflops=round(tflops, 1), padded_tflops=round(padded_flops / (us * 1e-6) / 1e12, 1),
+                algorithmic_bytes=nbytes, algorithmic_gbps=round(gbps, 1),
+                roofline_us={"mfma_bf16": round(t_mfma, 2), "hbm": round(t_hbm, 2)},
+                bound="hbm" if t_hbm > t_mfma else "mfma",
+                frac_of_bound=round(max(t_mfma, t_hbm) / us, 4))
+
+
 def traffic_record(kernel, workload):
     """HBM traffic per launch measured with rocprofv3 PMC counters and stored
     under profiles/, used only while the kernel source still has the hash the
@@ -273,6 +320,12 @@ def main():
         extra["sort_from_ids_" + cfg.name] = so
         log(f"[bench] sort_from_ids on {cfg.name} ids: {so['us_per_call']:.2f} us/call, "
             f"{so['routes_per_s']:.3e} routes/s")
+        gm = time_gemm1(cfg, 20, torch, amr)
+        extra["grouped_gemm1_" + cfg.name] = gm
+        log(f"[bench] grouped GEMM1 (K={gm['K']}, N={gm['N']}) on {cfg.name} metadata: {gm['us_per_call']:.1f} us, "
+            f"{gm['useful_tflops']:.1f} TFLOP/s routed ({gm['padded_tflops']:.1f} with padding), "
+            f"{gm['active_experts']} experts active, {gm['algorithmic_gbps']:.0f} GB/s, "
+            f"{gm['frac_of_bound']:.3f} of the {gm['bound']} bound")
 
     cpu = None
     if not args.no_cpu_baseline:
