@@ -756,25 +756,34 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
       // every load of the lane run is issued before the first use (a load past
       // the run repeats the last vector, which stays inside the row)
       constexpr int NQ = EPLM >= PER ? EPLM / PER : 0;
+      // runs of more than 32 FP32 logits arrive in two batches, so the raw
+      // vectors and the keys do not need registers for the whole run at once
+      constexpr int NB = (!BF16 && NQ > 8) ? 2 : 1;
+      constexpr int QB = NQ > 0 ? NQ / NB : 1;
       const int nq = epl / PER;
-      uint4 raw[NQ > 0 ? NQ : 1];
+      uint4 raw[QB];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) raw[q] = src[min(q, nq - 1)];
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        if (q < nq) {
-          if constexpr (BF16) {
-            put_pair(q * 8 + 0, raw[q].x);
-            put_pair(q * 8 + 2, raw[q].y);
-            put_pair(q * 8 + 4, raw[q].z);
-            put_pair(q * 8 + 6, raw[q].w);
-          } else {
-            put(q * 4 + 0, __uint_as_float(raw[q].x));
-            put(q * 4 + 1, __uint_as_float(raw[q].y));
-            put(q * 4 + 2, __uint_as_float(raw[q].z));
-            put(q * 4 + 3, __uint_as_float(raw[q].w));
+        for (int q = 0; q < QB; ++q) raw[q] = src[min(b * QB + q, nq - 1)];
+#pragma unroll
+        for (int qq = 0; qq < QB; ++qq) {
+          const int q = b * QB + qq;
+          if (q < nq) {
+            if constexpr (BF16) {
+              put_pair(q * 8 + 0, raw[qq].x);
+              put_pair(q * 8 + 2, raw[qq].y);
+              put_pair(q * 8 + 4, raw[qq].z);
+              put_pair(q * 8 + 6, raw[qq].w);
+            } else {
+              put(q * 4 + 0, __uint_as_float(raw[qq].x));
+              put(q * 4 + 1, __uint_as_float(raw[qq].y));
+              put(q * 4 + 2, __uint_as_float(raw[qq].z));
+              put(q * 4 + 3, __uint_as_float(raw[qq].w));
+            }
           }
         }
+        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -1500,7 +1509,9 @@ typedef void (*KernelFn)(Args);
 
 // Experts per lane compiled as constants (straight-line code).  With 64-lane
 // segments any other value runs the variant that reads it at run time; 32-lane
-// segments are used only for the listed values.  A lane run that is a whole
+// segments are used only for the listed values.  FP32 rows with 64 experts per
+// lane also take the run-time variant: the constant one needs more registers
+// than a lane has at 16 waves per compute unit and measured slower.  A lane run that is a whole
 // number of 16-byte vectors loads straight from HBM (LOAD_VEC), otherwise the
 // rows go through the wave's LDS staging buffers (LOAD_STAGE).
 constexpr bool vec_mode(int epl, bool bf16) { return (epl * (bf16 ? 2 : 4)) % 16 == 0; }
@@ -1532,7 +1543,9 @@ bool seg32_epl(int epl) {
       case 14: return fix_##KER<64, 14, BF16>();                                                   \
       case 16: return fix_##KER<64, 16, BF16>();                                                   \
       case 32: return fix_##KER<64, 32, BF16>();                                                   \
-      case 64: return fix_##KER<64, 64, BF16>();                                                   \
+      case 64:                                                                                     \
+        if constexpr (BF16) return fix_##KER<64, 64, BF16>();                                      \
+        [[fallthrough]];                                                                           \
       default: return mode == LOAD_VEC ? KER<64, 0, BF16, LOAD_VEC> : KER<64, 0, BF16, LOAD_STAGE>; \
     }                                                                                              \
   }                                                                                                \
