@@ -223,6 +223,18 @@ def sort_metadata(ids: np.ndarray, E: int, block: int) -> SortMeta:
                     sorted_ids.astype(np.int32), expert_of_block.astype(np.int32))
 
 
+def local_metadata(ids: np.ndarray, local_begin: int, local_count: int, block: int) -> SortMeta:
+    """Sort metadata of one expert-parallel rank that owns experts
+    [local_begin, local_begin + local_count), numbered from 0 there.  A route
+    to another rank's expert claims no row here, like a dropped route (page
+    "gfx1250 ordinary-TP route optimization", Dispatch and contracts); the
+    sentinel stays M*k."""
+    ids = np.asarray(ids, dtype=np.int64)
+    rel = ids - local_begin
+    rel = np.where((rel >= 0) & (rel < local_count), rel, -1)
+    return sort_metadata(rel, local_count, block)
+
+
 # ---------------------------------------------------------------------------
 # The whole path.
 # ---------------------------------------------------------------------------

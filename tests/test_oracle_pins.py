@@ -443,3 +443,38 @@ def test_oracle_end_to_end_tiny_invariants():
     assert orc.check_selection_invariants(r.keys, r.ids, cfg.n_group, cfg.topk_group) == []
     assert orc.check_sort_invariants(r.ids, r.meta.sorted_ids, r.meta.expert_of_block,
                                      r.meta.num_post_pad, cfg.E, cfg.block) == []
+
+
+# ---------------------------------------------------------------------------
+# Expert-parallel local metadata
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,E,k,block,ranks", [(50, 64, 4, 8, 4), (7, 12, 3, 1, 3), (200, 896, 16, 128, 8)])
+def test_local_metadata_partitions_the_global_metadata(M, E, k, block, ranks):
+    # each rank's rows are exactly the global rows of its experts, in the same
+    # order, and the ranks' counts add up to the global ones
+    rng = np.random.default_rng(M + E)
+    ids = np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(M)]).astype(np.int32)
+    g = orc.sort_metadata(ids, E, block)
+    EL = E // ranks
+    total = 0
+    for r in range(ranks):
+        m = orc.local_metadata(ids, r * EL, EL, block)
+        assert np.array_equal(m.counts, g.counts[r * EL:(r + 1) * EL])
+        lo, hi = g.offsets[r * EL], (g.offsets[(r + 1) * EL] if (r + 1) * EL < E else g.num_post_pad)
+        assert np.array_equal(m.sorted_ids, g.sorted_ids[lo:hi])
+        assert np.array_equal(m.expert_of_block + r * EL, g.expert_of_block[lo // block:hi // block])
+        total += int(m.counts.sum())
+    assert total == M * k
+
+
+def test_local_metadata_small_example():
+    # two tokens, k = 2, experts 0..3, the rank owns experts 1 and 2
+    ids = np.array([[1, 3], [0, 1]], dtype=np.int32)
+    m = orc.local_metadata(ids, 1, 2, 2)
+    # expert 1 (local 0) takes slots 0 and 3; expert 2 (local 1) takes none
+    assert m.num_post_pad == 2
+    assert m.sorted_ids.tolist() == [0, 3]
+    assert m.expert_of_block.tolist() == [0]
+    full = orc.local_metadata(ids, 0, 4, 2)
+    g = orc.sort_metadata(ids, 4, 2)
+    assert np.array_equal(full.sorted_ids, g.sorted_ids) and np.array_equal(full.expert_of_block, g.expert_of_block)
