@@ -33,6 +33,7 @@ EXPORTED = [
     "moe_route_sort",
     "moe_route_sort_ex",
     "moe_route_sort_profiled",
+    "moe_route_sort_local",
     "moe_sort_from_ids",
     "moe_route_sort_max_rows",
     "moe_route_sort_max_blocks",
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_ex.restype = i32
     L.moe_route_sort_profiled.argtypes = common + [ctypes.c_uint, vp, vp, vp]
     L.moe_route_sort_profiled.restype = i32
+    L.moe_route_sort_local.argtypes = common[:8] + [i32, i32] + common[8:]
+    L.moe_route_sort_local.restype = i32
     L.moe_sort_from_ids.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_sort_from_ids.restype = i32
     for name in ("moe_route_sort_max_rows", "moe_route_sort_max_blocks"):
@@ -142,7 +145,7 @@ def _workspace(device, nbytes: int):
 
 def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
                out: Optional[RouteSortOutput] = None, workspace=None, flags: int = 0,
-               stats=None, stream=None, events=None) -> RouteSortOutput:
+               stats=None, stream=None, events=None, local=None) -> RouteSortOutput:
     """Run the route-sort path on the GPU.
 
     logits: [M, E] float32 or bfloat16 CUDA/HIP tensor, contiguous.
@@ -155,6 +158,10 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             2i and 2i+1 take the start and end of the call's kernel i (pairs
             past the last kernel are recorded after it); returns
             (output, launches) then.
+    local:  optional (begin, count): metadata only for experts
+            [begin, begin + count), numbered from 0 (moe_route_sort_local);
+            ids and weights stay global.  Not combined with flags, stats or
+            events.
     """
     import torch
     if not (isinstance(logits, torch.Tensor) and logits.is_cuda):
@@ -172,8 +179,15 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             bias.dtype == torch.float32 and bias.shape == (E,) and bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 [E] tensor on the logits' device")
     dev = logits.device
-    rows = max_rows(M, E, k, block)
-    blocks = max_blocks(M, E, k, block)
+    if local is not None:
+        lb, lc = (int(v) for v in local)
+        if not (0 <= lb and 1 <= lc and lb + lc <= E):
+            raise ValueError("local range must lie inside [0, E) and hold at least one expert")
+        if flags or stats is not None or events is not None:
+            raise ValueError("a local range is not combined with flags, stats or events")
+    EL = E if local is None else lc
+    rows = max_rows(M, EL, k, block)
+    blocks = max_blocks(M, EL, k, block)
     if rows < 0:
         raise ValueError("invalid sizes or row capacity overflow")
     if out is None:
@@ -199,6 +213,14 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if local is not None:
+        rc = int(lib().moe_route_sort_local(
+            logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block, lb, lc,
+            out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
+            out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt, ws_ptr, ws_len, stream.cuda_stream))
+        if rc != MRS_OK:
+            raise RouteSortError(rc)
+        return out
     args = (logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block,
             out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
             out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt, ws_ptr, ws_len,

@@ -108,6 +108,7 @@ struct Args {
   int32_t* ws_slot;  // [M*k] expert | (rank inside the workgroup << 16)
   int32_t* stats;
   const int32_t* in_ids;  // sort-only entry: caller's expert ids [M, k]
+  int e_lo, EL;  // experts [e_lo, e_lo + EL) get metadata (all E unless a local range is asked for)
 };
 
 // ----------------------------------------------------------------------------
@@ -1082,14 +1083,14 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
 // Exclusive scan of padded counts over all experts into L.off; returns the
 // total (in every thread).  `padded(e)` gives expert e's padded count.
 template <typename F>
-__device__ int expert_offsets(const Args& a, const Lds& L, F padded) {
+__device__ int expert_offsets(const Args& a, const Lds& L, int n, F padded) {
   const int tid = threadIdx.x;
-  const int ept = (a.E + kWG - 1) / kWG;
+  const int ept = (n + kWG - 1) / kWG;
   const int e0 = tid * ept;
   int local = 0;
   for (int i = 0; i < ept; ++i) {
     const int e = e0 + i;
-    if (e < a.E) {
+    if (e < n) {
       const int p = padded(e);
       L.off[e] = p;
       local += p;
@@ -1098,7 +1099,7 @@ __device__ int expert_offsets(const Args& a, const Lds& L, F padded) {
   int pre = wg_excl_scan(L, local);
   for (int i = 0; i < ept; ++i) {
     const int e = e0 + i;
-    if (e < a.E) {
+    if (e < n) {
       const int p = L.off[e];
       L.off[e] = pre;
       pre += p;
@@ -1118,11 +1119,13 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
   select_tokens<SEG, EPL, BF16, MODE>(a, L, 0, a.M);
   const int tid = threadIdx.x;
-  const int total = expert_offsets(a, L, [&](int e) { return pad_block(__popcll(L.bits[e]), a); });
+  // metadata of experts [e_lo, e_lo + EL), numbered from 0
+  const unsigned long long* bits = L.bits + a.e_lo;
+  const int total = expert_offsets(a, L, a.EL, [&](int e) { return pad_block(__popcll(bits[e]), a); });
   if (tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
-  for (int e = tid; e < a.E; e += kWG) {
-    const int c = __popcll(L.bits[e]);
+  for (int e = tid; e < a.EL; e += kWG) {
+    const int c = __popcll(bits[e]);
     const int p = pad_block(c, a);
     const int o = L.off[e];
     for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
@@ -1130,9 +1133,11 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   }
   for (int q = tid; q < sentinel; q += kWG) {
     const int tl = q / a.k;
-    const int e = L.ids[q];
-    const int rank = __popcll(L.bits[e] & ((1ull << tl) - 1ull));
-    a.sorted_ids[L.off[e] + rank] = q;
+    const int e = L.ids[q] - a.e_lo;
+    if ((unsigned)e < (unsigned)a.EL) {
+      const int rank = __popcll(bits[e] & ((1ull << tl) - 1ull));
+      a.sorted_ids[L.off[e] + rank] = q;
+    }
   }
 }
 
@@ -1145,14 +1150,17 @@ __global__ __launch_bounds__(kWG) void k_select(Args a) {
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
   select_tokens<SEG, EPL, BF16, MODE>(a, L, t0, nt);
-  for (int e = threadIdx.x; e < a.E; e += kWG)
-    a.ws_hist[(size_t)w * a.E + e] = __popcll(L.bits[e]);
+  // histogram row and slot records over experts [e_lo, e_lo + EL), numbered
+  // from 0; a pick outside that range is recorded as a dropped route (-1)
+  const unsigned long long* bits = L.bits + a.e_lo;
+  for (int e = threadIdx.x; e < a.EL; e += kWG)
+    a.ws_hist[(size_t)w * a.EL + e] = __popcll(bits[e]);
   const int ns = nt * a.k;
   int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
   for (int q = threadIdx.x; q < ns; q += kWG) {
     const int tl = q / a.k;
-    const int e = L.ids[q];
-    rec[q] = e | (__popcll(L.bits[e] & ((1ull << tl) - 1ull)) << 16);
+    const int e = L.ids[q] - a.e_lo;
+    rec[q] = (unsigned)e < (unsigned)a.EL ? (e | (__popcll(bits[e] & ((1ull << tl) - 1ull)) << 16)) : -1;
   }
 }
 
@@ -1661,7 +1669,7 @@ size_t moe_route_sort_workspace_bytes(int M, int E, int k, int block) {
 }
 
 static int route_sort_impl(const void* logits, const float* bias, int M, int E, int k, int n_group,
-                           int topk_group, int block, int32_t* out_ids, float* out_w,
+                           int topk_group, int block, int e_lo, int EL, int32_t* out_ids, float* out_w,
                            int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
                            int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
                            unsigned flags, int32_t* stats, Timing* tm) {
@@ -1670,9 +1678,10 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && (flags & MRS_FLAG_FORCE_MULTI_WG)) return MRS_ERR_INVALID_ARG;
   if (!valid_sizes(M, E, k, block) || n_group < 1 || E % n_group != 0 || topk_group < 1 ||
       topk_group > n_group || (int64_t)k > (int64_t)topk_group * (E / n_group) ||
-      (logits_dtype != MRS_DTYPE_F32 && logits_dtype != MRS_DTYPE_BF16))
+      (logits_dtype != MRS_DTYPE_F32 && logits_dtype != MRS_DTYPE_BF16) || e_lo < 0 || EL < 1 ||
+      e_lo > E - EL)
     return MRS_ERR_INVALID_ARG;
-  if ((int64_t)M * k > INT32_MAX || max_rows_of(M, E, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if ((int64_t)M * k > INT32_MAX || max_rows_of(M, EL, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
   if (num_post_pad == nullptr) return MRS_ERR_NULL_POINTER;
   if (!aligned(num_post_pad, 4)) return MRS_ERR_MISALIGNED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1691,6 +1700,8 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   a.bias = bias;
   a.M = M;
   a.E = E;
+  a.e_lo = e_lo;
+  a.EL = EL;
   a.k = k;
   a.n_group = n_group;
   a.topk_group = topk_group;
@@ -1788,9 +1799,13 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   const void* fsel = reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode));
   if (a.tbl && !no_static_lds(fsel)) return MRS_ERR_LAUNCH;
   int rc = launch(fsel, a.nwg, kWG, lds_sel, st, p_one, tm);
+  // the sort phases see only the experts that get metadata
+  Args as = a;
+  as.E = EL;
+  void* p_sort[] = {&as};
   if (rc == MRS_OK)
-    rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kWave - 1) / kWave, kWG, 0, st, p_one, tm);
-  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, tm);
+    rc = launch(reinterpret_cast<const void*>(k_colscan), (EL + kWave - 1) / kWave, kWG, 0, st, p_sort, tm);
+  if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_sort, tm);
   return rc;
 }
 
@@ -1799,7 +1814,7 @@ int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k
                       int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
                       int logits_dtype, void* workspace, size_t workspace_bytes, void* stream,
                       unsigned flags, int32_t* stats) {
-  return route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
+  return route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, 0, E, out_ids, out_w, sorted_ids,
                          expert_of_block, num_post_pad, logits_dtype, workspace, workspace_bytes, stream, flags,
                          stats, nullptr);
 }
@@ -1815,9 +1830,9 @@ int moe_route_sort_profiled(const void* logits, const float* bias, int M, int E,
     if (!events[i]) return MRS_ERR_NULL_POINTER;
     tm.ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
   }
-  const int rc = route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
-                                 expert_of_block, num_post_pad, logits_dtype, workspace, workspace_bytes, stream,
-                                 flags, stats, &tm);
+  const int rc = route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, 0, E, out_ids, out_w,
+                                 sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
+                                 workspace_bytes, stream, flags, stats, &tm);
   *n_launches = tm.n;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   for (int i = 2 * tm.n; rc == MRS_OK && i < 2 * kMaxLaunches; ++i)
@@ -1832,6 +1847,15 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
   return moe_route_sort_ex(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
                            sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
                            workspace_bytes, stream, 0u, nullptr);
+}
+
+int moe_route_sort_local(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                         int topk_group, int block, int local_begin, int local_count, int32_t* out_ids,
+                         float* out_w, int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                         int logits_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, local_begin, local_count, out_ids,
+                         out_w, sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
+                         workspace_bytes, stream, 0u, nullptr, nullptr);
 }
 
 int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_t* sorted_ids,

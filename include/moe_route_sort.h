@@ -139,6 +139,33 @@ int moe_route_sort_profiled(const void* logits, const float* bias, int M, int E,
                             unsigned flags, int32_t* stats, void* const* events, int* n_launches);
 
 /*
+ * moe_route_sort_local -- moe_route_sort for a rank that owns only the experts
+ * [local_begin, local_begin + local_count) (expert parallelism).  The pages
+ * keep expert-parallel routing as its own dispatch path (page "gfx1250
+ * ordinary-TP route optimization", Capacity and dispatch; Dispatch and
+ * contracts) and treat a route that claims no slot as dropped; this entry
+ * applies that to routes whose expert another rank owns.
+ *
+ *   The selection is the full one: out_ids / out_w hold the k global expert
+ *   ids and weights of every token, exactly as moe_route_sort writes them.
+ *   The metadata covers the local experts only, numbered from 0: sorted_ids
+ *   holds the slots t*k + j whose expert lies in the range (ascending within
+ *   an expert, sentinel M*k in the padding), expert_of_block holds
+ *   expert - local_begin, num_post_pad the local padded total.  A slot routed
+ *   to another rank's expert does not appear in sorted_ids.
+ *   Capacities: sorted_ids >= moe_route_sort_max_rows(M, local_count, k, block),
+ *   expert_of_block >= moe_route_sort_max_blocks(M, local_count, k, block).
+ *   Workspace: moe_route_sort_workspace_bytes(M, E, k, block).
+ *   0 <= local_begin, 1 <= local_count, local_begin + local_count <= E, else
+ *   MRS_ERR_INVALID_ARG; everything else as for moe_route_sort.
+ * With local_begin = 0 and local_count = E the result is moe_route_sort's.
+ */
+int moe_route_sort_local(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                         int topk_group, int block, int local_begin, int local_count, int32_t* out_ids,
+                         float* out_w, int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
+                         int logits_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_sort_from_ids -- the two sort phases alone, from expert ids chosen
  * elsewhere (page "gfx1250 ordinary-TP route optimization", Summary and
  * Dispatch and contracts: route rows built from selected ids with workgroup

@@ -197,3 +197,25 @@ def test_grouped_gemm1_checks():
     L = amr.lib()
     assert L.moe_grouped_gemm1_profiled(P, P, Q, Q, Q, 64, 8, 64, 256, 256, 64, P, None, None, None) == \
         amr.MRS_ERR_NULL_POINTER
+
+
+def local_call(**kw):
+    L = amr.lib()
+    d = dict(logits=P, bias=P, M=64, E=64, k=4, ng=8, tg=4, block=16, lb=0, lc=64, ids=Q, w=Q, rows=Q, eob=Q,
+             npp=Q, dtype=amr.MRS_DTYPE_F32, ws=Q, ws_bytes=1 << 20)
+    d.update(kw)
+    return L.moe_route_sort_local(d["logits"], d["bias"], d["M"], d["E"], d["k"], d["ng"], d["tg"], d["block"],
+                                  d["lb"], d["lc"], d["ids"], d["w"], d["rows"], d["eob"], d["npp"], d["dtype"],
+                                  d["ws"], d["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(lb=-1), dict(lc=0), dict(lb=60, lc=5), dict(lb=64, lc=1), dict(lc=65),
+                                dict(E=0), dict(k=0)])
+def test_local_invalid_ranges(kw):
+    assert local_call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_local_checks():
+    assert local_call(npp=None) == amr.MRS_ERR_NULL_POINTER
+    assert local_call(logits=None) == amr.MRS_ERR_NULL_POINTER
+    assert local_call(logits=P + 4) == amr.MRS_ERR_MISALIGNED
