@@ -172,6 +172,35 @@ def time_sort_from_ids(cfg, steps, torch, amr):
                 algorithmic_gbps=round(nbytes / (ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
 
 
+def time_local(cfg, steps, ranks, torch, amr):
+    """One expert-parallel rank's call (experts [0, E/ranks)) on this workload,
+    timed like the main loop (graph replay of consecutive calls)."""
+    inp = workloads.make_inputs(cfg)
+    x0, b = to_gpu(inp, torch)
+    rng_ = (0, cfg.E // ranks)
+    out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, local=rng_)
+    torch.cuda.synchronize()
+    G = graph_size(steps)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(G):
+            amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, local=rng_, out=out)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps // G):
+            graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return dict(ranks=ranks, local_experts=cfg.E // ranks, us_per_call=round(ms * 1e3, 3),
+                routes_per_s=cfg.M * cfg.k / (ms * 1e-3), local_rows=int(out.num_post_pad.item()))
+
+
 GEMM_K, GEMM_N = 3584, 768     # Kimi-K3 TP8 routed MoE: hidden 3584, 2 x intermediate 384
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 
@@ -320,6 +349,10 @@ def main():
         extra["sort_from_ids_" + cfg.name] = so
         log(f"[bench] sort_from_ids on {cfg.name} ids: {so['us_per_call']:.2f} us/call, "
             f"{so['routes_per_s']:.3e} routes/s")
+        lo = time_local(cfg, max(20, args.steps // 4), 8, torch, amr)
+        extra["local_rank_of_8_" + cfg.name] = lo
+        log(f"[bench] one rank of 8 (experts [0, {lo['local_experts']})) on {cfg.name}: "
+            f"{lo['us_per_call']:.2f} us/call, {lo['local_rows']} local rows")
         gm = time_gemm1(cfg, 20, torch, amr)
         extra["grouped_gemm1_" + cfg.name] = gm
         log(f"[bench] grouped GEMM1 (K={gm['K']}, N={gm['N']}) on {cfg.name} metadata: {gm['us_per_call']:.1f} us, "
