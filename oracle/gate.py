@@ -79,7 +79,7 @@ def midpoint_margin(hidden_bits: np.ndarray, w_bits: np.ndarray, logits: np.ndar
     h = bf16_to_f64(hidden_bits)
     w = bf16_to_f64(w_bits)
     absd = np.abs(h) @ np.abs(w).T                       # [M, E]
-    exact = h @ w.T                                      # float64, error << FP32 ulp
+    exact = np.array([[math.fsum(w[e] * h[t]) for e in range(w.shape[0])] for t in range(h.shape[0])])
     r = logits.astype(np.float32)
     up = np.nextafter(r, np.float32(np.inf)).astype(np.float64)
     dn = np.nextafter(r, np.float32(-np.inf)).astype(np.float64)

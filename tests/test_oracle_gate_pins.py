@@ -60,6 +60,15 @@ def test_matches_float64_product_within_its_bound(seed):
     ref = h @ w.T
     bound = H * 2.0 ** -53 * (np.abs(h) @ np.abs(w).T) + 2.0 ** -24 * np.abs(ref)
     assert np.all(np.abs(got - ref) <= bound)
-    # and no exact value lies within a float64 accumulation's error bound of a
-    # rounding midpoint, so such a kernel must round every logit the same way
-    assert np.all(og.midpoint_margin(hb, wb, og.gate_logits(hb, wb)) > H * 2.0 ** -53)
+
+
+def test_midpoint_margin_of_a_constructed_tie():
+    # exact value 1 + 2^-24 + 2^-70: distance 2^-70 from the midpoint 1 + 2^-24
+    h = _bits([[1.0, 2.0 ** -24, 2.0 ** -70]])
+    w = _bits([[1.0, 1.0, 1.0]])
+    m = og.midpoint_margin(h, w, og.gate_logits(h, w))
+    assert m[0, 0] < 2.0 ** -60
+    # a value far from any midpoint: 1 + 2^-25 sits a quarter ulp from both
+    h2 = _bits([[1.0, 2.0 ** -25]])
+    m2 = og.midpoint_margin(h2, _bits([[1.0, 1.0]]), og.gate_logits(h2, _bits([[1.0, 1.0]])))
+    assert abs(m2[0, 0] * (1.0 + 2.0 ** -25) - 2.0 ** -25) < 2.0 ** -50
