@@ -43,6 +43,7 @@ EXPORTED = [
     "moe_route_sort_sigmoid_table_probe",
     "moe_grouped_gemm1",
     "moe_grouped_gemm1_profiled",
+    "moe_gate_route_sort",
 ]
 
 _lib = None
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_gemm1.restype = i32
     L.moe_grouped_gemm1_profiled.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     L.moe_grouped_gemm1_profiled.restype = i32
+    L.moe_gate_route_sort.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_gate_route_sort.restype = i32
     _lib = L
     return L
 
@@ -363,3 +366,50 @@ def grouped_gemm1(x, w, sorted_ids, expert_of_block, num_post_pad, k: int, block
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return out
+
+
+def gate_route_sort(hidden, w_gate, bias, k: int, n_group: int, topk_group: int, block: int, *,
+                    out: Optional[RouteSortOutput] = None, logits=None, stream=None):
+    """Router gate projection then the route-sort path (include/moe_gate.h).
+
+    hidden: [M, H] bfloat16 (M <= 64), w_gate: [E, H] bfloat16, bias: [E]
+    float32, all on one GPU.  Returns (logits [M, E] float32, RouteSortOutput)."""
+    import torch
+    if not (isinstance(hidden, torch.Tensor) and hidden.is_cuda and hidden.dtype == torch.bfloat16 and
+            hidden.dim() == 2 and hidden.is_contiguous()):
+        raise ValueError("hidden must be a contiguous bfloat16 [M, H] GPU tensor")
+    if not (isinstance(w_gate, torch.Tensor) and w_gate.device == hidden.device and
+            w_gate.dtype == torch.bfloat16 and w_gate.dim() == 2 and w_gate.is_contiguous()):
+        raise ValueError("w_gate must be a contiguous bfloat16 [E, H] tensor on hidden's device")
+    M, H = hidden.shape
+    E = w_gate.shape[0]
+    if w_gate.shape[1] != H:
+        raise ValueError("hidden and w_gate disagree on H")
+    if not (isinstance(bias, torch.Tensor) and bias.device == hidden.device and bias.dtype == torch.float32 and
+            bias.shape == (E,) and bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [E] tensor on hidden's device")
+    dev = hidden.device
+    rows, blocks = max_rows(M, E, k, block), max_blocks(M, E, k, block)
+    if rows < 0:
+        raise ValueError("invalid sizes or row capacity overflow")
+    if logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    elif not (logits.dtype == torch.float32 and tuple(logits.shape) == (M, E) and logits.is_contiguous() and
+              logits.device == dev):
+        raise ValueError("logits must be a contiguous float32 [M, E] tensor on hidden's device")
+    if out is None:
+        out = RouteSortOutput(torch.empty((M, k), dtype=torch.int32, device=dev),
+                              torch.empty((M, k), dtype=torch.float32, device=dev),
+                              torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
+                              torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
+                              torch.empty((1,), dtype=torch.int32, device=dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = int(lib().moe_gate_route_sort(hidden.data_ptr(), w_gate.data_ptr(), bias.data_ptr(), M, E, H, k, n_group,
+                                       topk_group, block, logits.data_ptr(), out.ids.data_ptr(),
+                                       out.weights.data_ptr(), out.sorted_ids.data_ptr(),
+                                       out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(),
+                                       stream.cuda_stream))
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return logits, out

@@ -5,7 +5,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "moe_route_sort.hip"), os.path.join(HERE, "csrc", "moe_gemm1.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("moe_route_sort.hip", "moe_gemm1.hip", "moe_gate.hip")]
 OUT = os.path.join(HERE, "libmoe_route_sort.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,7 +22,8 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", OUT + ".tmp"]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *SRCS,
+           "-o", OUT + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

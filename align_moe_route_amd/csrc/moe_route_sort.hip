@@ -55,6 +55,7 @@
 #include <type_traits>
 
 #include "moe_route_sort.h"
+#include "route_internal.h"
 
 namespace {
 
@@ -345,15 +346,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
   u = max(u, dpp<kRowShr8>(0u, u));
   u = max(u, dpp<kRowBcast15, 0xA>(0u, u));
   u = max(u, dpp<kRowBcast31, 0xC>(0u, u));
-  return readlane(u, 63);
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t u) {
-  u = min(u, dpp<kRowShr1>(0xFFFFFFFFu, u));
-  u = min(u, dpp<kRowShr2>(0xFFFFFFFFu, u));
-  u = min(u, dpp<kRowShr4>(0xFFFFFFFFu, u));
-  u = min(u, dpp<kRowShr8>(0xFFFFFFFFu, u));
-  u = min(u, dpp<kRowBcast15, 0xA>(0xFFFFFFFFu, u));
-  u = min(u, dpp<kRowBcast31, 0xC>(0xFFFFFFFFu, u));
   return readlane(u, 63);
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -1634,6 +1626,25 @@ int ensure_sig_table(hipStream_t st) {
 
 }  // namespace
 
+int mrs_check_route_args(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                         int topk_group, int block, const int32_t* out_ids, const float* out_w,
+                         const int32_t* sorted_ids, const int32_t* expert_of_block,
+                         const int32_t* num_post_pad, int logits_dtype) {
+  if (!valid_sizes(M, E, k, block) || n_group < 1 || E % n_group != 0 || topk_group < 1 ||
+      topk_group > n_group || (int64_t)k > (int64_t)topk_group * (E / n_group) ||
+      (logits_dtype != MRS_DTYPE_F32 && logits_dtype != MRS_DTYPE_BF16))
+    return MRS_ERR_INVALID_ARG;
+  if ((int64_t)M * k > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if (num_post_pad == nullptr) return MRS_ERR_NULL_POINTER;
+  if (!aligned(num_post_pad, 4)) return MRS_ERR_MISALIGNED;
+  if (M == 0) return MRS_OK;  // only num_post_pad is written
+  if (!logits || !bias || !out_ids || !out_w || !sorted_ids || !expert_of_block) return MRS_ERR_NULL_POINTER;
+  if (!aligned(logits, 16) || !aligned(bias, 4) || !aligned(out_ids, 4) || !aligned(out_w, 4) ||
+      !aligned(sorted_ids, 4) || !aligned(expert_of_block, 4))
+    return MRS_ERR_MISALIGNED;
+  return MRS_OK;
+}
+
 // ----------------------------------------------------------------------------
 // C ABI.
 // ----------------------------------------------------------------------------
@@ -1676,24 +1687,19 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   const unsigned known = MRS_FLAG_FORCE_SINGLE_WG | MRS_FLAG_FORCE_MULTI_WG | MRS_FLAG_FORCE_EXACT;
   if ((flags & ~known) != 0u) return MRS_ERR_INVALID_ARG;
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && (flags & MRS_FLAG_FORCE_MULTI_WG)) return MRS_ERR_INVALID_ARG;
-  if (!valid_sizes(M, E, k, block) || n_group < 1 || E % n_group != 0 || topk_group < 1 ||
-      topk_group > n_group || (int64_t)k > (int64_t)topk_group * (E / n_group) ||
-      (logits_dtype != MRS_DTYPE_F32 && logits_dtype != MRS_DTYPE_BF16) || e_lo < 0 || EL < 1 ||
-      e_lo > E - EL)
-    return MRS_ERR_INVALID_ARG;
-  if ((int64_t)M * k > INT32_MAX || max_rows_of(M, EL, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
-  if (num_post_pad == nullptr) return MRS_ERR_NULL_POINTER;
-  if (!aligned(num_post_pad, 4)) return MRS_ERR_MISALIGNED;
+  if (e_lo < 0 || EL < 1 || e_lo > E - EL) return MRS_ERR_INVALID_ARG;
+  {
+    const int rc = mrs_check_route_args(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
+                                        sorted_ids, expert_of_block, num_post_pad, logits_dtype);
+    if (rc != MRS_OK) return rc;
+  }
+  if (max_rows_of(M, EL, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if (stats && !aligned(stats, 4)) return MRS_ERR_MISALIGNED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (M == 0) {
     void* params[] = {&num_post_pad};
     return launch(reinterpret_cast<const void*>(k_zero_npp), 1, 1, 0, st, params, tm);
   }
-  if (!logits || !bias || !out_ids || !out_w || !sorted_ids || !expert_of_block)
-    return MRS_ERR_NULL_POINTER;
-  if (!aligned(logits, 16) || !aligned(bias, 4) || !aligned(out_ids, 4) || !aligned(out_w, 4) ||
-      !aligned(sorted_ids, 4) || !aligned(expert_of_block, 4) || (stats && !aligned(stats, 4)))
-    return MRS_ERR_MISALIGNED;
 
   Args a{};
   a.logits = logits;

@@ -219,3 +219,25 @@ def test_local_checks():
     assert local_call(npp=None) == amr.MRS_ERR_NULL_POINTER
     assert local_call(logits=None) == amr.MRS_ERR_NULL_POINTER
     assert local_call(logits=P + 4) == amr.MRS_ERR_MISALIGNED
+
+
+def gate_call(**kw):
+    L = amr.lib()
+    d = dict(h=P, w=P, bias=Q, M=1, E=896, H=7168, k=16, ng=8, tg=4, block=32, logits=P, ids=Q, wt=Q, rows=Q,
+             eob=Q, npp=Q)
+    d.update(kw)
+    return L.moe_gate_route_sort(d["h"], d["w"], d["bias"], d["M"], d["E"], d["H"], d["k"], d["ng"], d["tg"],
+                                 d["block"], d["logits"], d["ids"], d["wt"], d["rows"], d["eob"], d["npp"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(M=65), dict(H=0), dict(H=12), dict(E=0), dict(E=900),
+                                dict(k=0), dict(tg=9), dict(block=0)])
+def test_gate_invalid_arguments(kw):
+    assert gate_call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_gate_checks():
+    for name in ("h", "w", "bias", "logits", "ids", "wt", "rows", "eob", "npp"):
+        assert gate_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER, name
+    for name in ("h", "w", "logits"):
+        assert gate_call(**{name: P + 8}) == amr.MRS_ERR_MISALIGNED, name
