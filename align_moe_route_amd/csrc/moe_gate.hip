@@ -8,9 +8,9 @@
 //
 // At batch 1 the gate is a matrix-vector product: the E x H BF16 weight matrix
 // (12.8 MB for 896 experts and H = 7168) is read once and every weight is used
-// once per token, so it is bound by HBM, not by a matrix unit.  One wave per
-// expert streams its weight row in 16-byte vectors, multiplies by the tokens'
-// hidden rows (shared by all waves, so they stay in L2) and accumulates in
+// once per token, so it is bound by HBM, not by a matrix unit.  One workgroup
+// per expert streams its weight row in 16-byte vectors, multiplies by the
+// tokens' hidden rows (shared by all workgroups, so they stay in L2) and accumulates in
 // float64: every BF16 x BF16 product is exact there and the sum is far more
 // precise than FP32, so the one FP32 rounding at the end gives the correctly
 // rounded dot product except where it lies within ~2^-40 (relative) of an
@@ -26,7 +26,7 @@
 
 namespace {
 
-constexpr int kGateWaves = 4;   // waves (experts) per workgroup
+constexpr int kGateWaves = 4;   // waves per workgroup (one expert)
 constexpr int kGateTok = 4;     // tokens per pass over a weight row
 constexpr int kGateMaxM = 64;   // batch limit of this entry point
 
@@ -45,20 +45,24 @@ __device__ __forceinline__ void unpack8(const uint4 q, double* f) {
   }
 }
 
+// One workgroup per expert: its 256 threads split the weight row (thread i
+// takes vectors i, i + 256, ...), so a row's loads are all in flight at once;
+// the partial sums meet in LDS.
 __global__ __launch_bounds__(kGateWaves * 64) void k_gate(const uint16_t* __restrict__ hidden,
                                                           const uint16_t* __restrict__ w, float* logits, int M,
                                                           int E, int H) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kGateWaves + (threadIdx.x >> 6);
-  if (e >= E) return;  // the whole wave leaves
+  constexpr int kT = kGateWaves * 64;
+  __shared__ double part[kGateTok][kGateWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x;
   const int nv = H / 8;  // 16-byte vectors per row
   const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)e * H);
   for (int t0 = 0; t0 < M; t0 += kGateTok) {
     double acc[kGateTok];
 #pragma unroll
     for (int j = 0; j < kGateTok; ++j) acc[j] = 0.0;
-#pragma unroll 2
-    for (int c = lane; c < nv; c += 64) {
+#pragma unroll 4
+    for (int c = tid; c < nv; c += kT) {
       double wf[8];
       unpack8(wr[c], wf);
 #pragma unroll
@@ -74,8 +78,16 @@ __global__ __launch_bounds__(kGateWaves * 64) void k_gate(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < kGateTok; ++j) {
       const double s = wave_sum(acc[j]);
-      if (lane == 0 && t0 + j < M) logits[(size_t)(t0 + j) * E + e] = (float)s;
+      if (lane == 0) part[j][wv] = s;
     }
+    __syncthreads();
+    if (tid < kGateTok && t0 + tid < M) {
+      double s = 0.0;
+#pragma unroll
+      for (int q = 0; q < kGateWaves; ++q) s += part[tid][q];
+      logits[(size_t)(t0 + tid) * E + e] = (float)s;
+    }
+    __syncthreads();  // part is reused by the next pass
   }
 }
 
@@ -99,7 +111,7 @@ extern "C" int moe_gate_route_sort(const void* hidden, const void* w_gate, const
     const uint16_t* h16 = static_cast<const uint16_t*>(hidden);
     const uint16_t* w16 = static_cast<const uint16_t*>(w_gate);
     void* params[] = {&h16, &w16, &out_logits, &M, &E, &H};
-    const dim3 grid((unsigned)((E + kGateWaves - 1) / kGateWaves));
+    const dim3 grid((unsigned)E);
     if (hipLaunchKernel(reinterpret_cast<const void*>(k_gate), grid, dim3(kGateWaves * 64), params, 0, st) !=
         hipSuccess)
       return MRS_ERR_LAUNCH;

@@ -201,6 +201,42 @@ def time_local(cfg, steps, ranks, torch, amr):
                 routes_per_s=cfg.M * cfg.k / (ms * 1e-3), local_rows=int(out.num_post_pad.item()))
 
 
+GATE_H = 7168  # Kimi-K3 model hidden size
+
+
+def time_gate(steps, torch, amr):
+    """Batch-1 gate projection + route-sort (decode shape: 1 token, 896
+    experts, top-16, H = 7168), graph replay of consecutive calls, plus the
+    gate kernel alone timed by its own HIP events."""
+    cfg = workloads.CONFIGS["decode"]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    h = torch.randn((1, GATE_H), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((cfg.E, GATE_H), generator=g, device="cuda") * GATE_H ** -0.5).to(torch.bfloat16)
+    b = (torch.rand((cfg.E,), generator=g, device="cuda") * 0.2 - 0.1).float()
+    logits, out = amr.gate_route_sort(h, w, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    torch.cuda.synchronize()
+    G = graph_size(steps)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(G):
+            amr.gate_route_sort(h, w, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out, logits=logits)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps // G):
+            graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / steps * 1e3
+    wbytes = cfg.E * GATE_H * 2
+    return dict(M=1, E=cfg.E, H=GATE_H, k=cfg.k, us_per_call=round(us, 3), weight_bytes=wbytes,
+                weight_gbps_over_call=round(wbytes / (us * 1e-6) / 1e9, 1))
+
+
 GEMM_K, GEMM_N = 3584, 768     # Kimi-K3 TP8 routed MoE: hidden 3584, 2 x intermediate 384
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 
@@ -353,6 +389,10 @@ def main():
         extra["local_rank_of_8_" + cfg.name] = lo
         log(f"[bench] one rank of 8 (experts [0, {lo['local_experts']})) on {cfg.name}: "
             f"{lo['us_per_call']:.2f} us/call, {lo['local_rows']} local rows")
+        ga = time_gate(max(20, args.steps // 4), torch, amr)
+        extra["gate_route_sort_decode"] = ga
+        log(f"[bench] gate projection (H={ga['H']}) + route-sort, 1 token: {ga['us_per_call']:.2f} us/call "
+            f"({ga['weight_gbps_over_call']:.0f} GB/s of gate weights over the whole call)")
         gm = time_gemm1(cfg, 20, torch, amr)
         extra["grouped_gemm1_" + cfg.name] = gm
         log(f"[bench] grouped GEMM1 (K={gm['K']}, N={gm['N']}) on {cfg.name} metadata: {gm['us_per_call']:.1f} us, "
