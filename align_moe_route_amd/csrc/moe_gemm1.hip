@@ -6,13 +6,15 @@
 //
 // A workgroup (4 waves) computes a BM x 128 tile of y.  BM divides the padding
 // block, so the tile's rows all belong to one expert: expert_of_block gives
-// the weight matrix, sorted_ids gives the token of each row (padding rows read
-// nothing and produce zeros).  The K loop steps by 64: every thread fetches
+// the weight matrix, sorted_ids gives the token of each row (a padding row
+// stores zeros into LDS and so produces zeros).  The K loop steps by 64: every thread fetches
 // its 16-byte chunks of the next x and W tiles into registers while the waves
 // run v_mfma_f32_32x32x16_bf16 on the current LDS tiles, then stores them into
 // the other LDS buffer (one barrier per step).  LDS rows are XOR-swizzled by
-// 16-byte chunk so that the MFMA operand reads (32 rows at one chunk) spread
-// over all banks.  num_post_pad is read on the device: tiles past it exit.
+// 16-byte chunk (swz below).  The column tiles of one row tile run back to
+// back on one XCD (tile_of below), so its gathered rows of x are fetched into
+// that XCD's L2 once.  num_post_pad is read on the device: tiles past it
+// exit.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -41,12 +43,29 @@ struct GArgs {
   uint16_t* y;
   int M, k, E, K, N, block;
   int row_limit;  // rows the metadata can hold: (max_rows / block) * block
+  int nrt;        // row tiles: row_limit / BM
 };
 
-// LDS slot of chunk c of tile row r: the chunk index is XORed with r mod 8, so
-// eight consecutive rows read at one logical chunk hit eight distinct 16-byte
-// bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 7)); }
+// LDS slot of chunk c of tile row r (rows are 128 bytes): the chunk index is
+// XORed with r mod 8 and, for the second eight rows of every sixteen, with 1
+// as well.  Any eight rows starting at a multiple of 8 then read one logical
+// chunk from eight distinct 16-byte positions of a 128-byte bank line, and
+// any sixteen starting at a multiple of 16 from sixteen distinct positions of
+// a 256-byte line, so the MFMA operand reads (32 rows at one chunk) are free
+// of bank conflicts whether the LDS serves 128 or 256 bytes per cycle.
+__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 7) ^ ((r >> 3) & 1)); }
+
+// MI355X dispatches workgroup h to XCD h mod 8.  Workgroups h = 8 (ntn G + j)
+// + x, j < ntn, all run on XCD x and take row tile 8 G + x with column tile
+// j: the ntn column tiles of a row tile are dispatched one after another on
+// the same XCD.  Returns false for the padding workgroups of the last group.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool tile_of(int h, int ntn, int nrt, int& rt, int& ct) {
+  const int x = h % kXcds, j = (h / kXcds) % ntn, G = h / (kXcds * ntn);
+  rt = G * kXcds + x;
+  ct = j;
+  return rt < nrt;
+}
 
 // FP32 to BF16, round to nearest even (the inputs are finite).
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -69,14 +88,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int r0 = blockIdx.x * BM;
-  const int n0 = blockIdx.y * kBN;
+  int rt, ct;
+  if (!tile_of((int)blockIdx.x, g.N / kBN, g.nrt, rt, ct)) return;
+  const int r0 = rt * BM;
+  const int n0 = ct * kBN;
   const int npp = min(*g.npp, g.row_limit);
   if (r0 + BM > npp) return;  // npp is a multiple of block and BM divides block
   const int e = g.eob[r0 / g.block];
   if (e < 0 || e >= g.E) return;
 
   // sources of this thread's chunks: rows of x through sorted_ids, rows of W[e]
+  // (a padding row reads token 0's row and stores zeros instead, so every
+  // load is unconditional)
   const u32x4* xa[AP];
   bool av[AP];
   const int routes = g.M * g.k;
@@ -100,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GArgs g) {
   u32x4 ra[AP], rb[BP];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int p = 0; p < AP; ++p) ra[p] = av[p] ? xa[p][kt * kChunks] : u32x4{0u, 0u, 0u, 0u};
+    for (int p = 0; p < AP; ++p) ra[p] = xa[p][kt * kChunks];
 #pragma unroll
     for (int p = 0; p < BP; ++p) rb[p] = wb[p][kt * kChunks];
   };
@@ -108,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GArgs g) {
 #pragma unroll
     for (int p = 0; p < AP; ++p) {
       const int idx = tid + p * kThreads;
-      As[buf][swz(idx / kChunks, idx % kChunks)] = ra[p];
+      As[buf][swz(idx / kChunks, idx % kChunks)] = av[p] ? ra[p] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int p = 0; p < BP; ++p) {
@@ -182,12 +205,15 @@ int gemm1_impl(const void* x, const void* w, const int32_t* sorted_ids, const in
   const int64_t row_limit = max_rows / block * block;
   if (row_limit == 0) return MRS_OK;  // no token: nothing to write
   const int bm = block % 128 == 0 ? 128 : (block % 64 == 0 ? 64 : 32);
+  const int64_t nrt = row_limit / bm, ntn = N / kBN;
+  const int64_t groups = (nrt + kXcds - 1) / kXcds;
+  if (groups * kXcds * ntn > INT32_MAX) return MRS_ERR_OVERFLOW;
   GArgs g{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), sorted_ids, expert_of_block,
-          num_post_pad, static_cast<uint16_t*>(y), M, k, E, K, N, block, (int)row_limit};
+          num_post_pad, static_cast<uint16_t*>(y), M, k, E, K, N, block, (int)row_limit, (int)nrt};
   const void* fn = bm == 128 ? reinterpret_cast<const void*>(k_gemm1<128>)
                    : bm == 64 ? reinterpret_cast<const void*>(k_gemm1<64>)
                               : reinterpret_cast<const void*>(k_gemm1<32>);
-  const dim3 grid((unsigned)(row_limit / bm), (unsigned)(N / kBN));
+  const dim3 grid((unsigned)(groups * kXcds * ntn));
   void* params[] = {&g};
   hipError_t err;
   if (ev0 && ev1)
