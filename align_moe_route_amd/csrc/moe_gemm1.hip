@@ -4,13 +4,14 @@
 // directly (page "Kimi-K3 B1 route-sort + prepared-MoE handoff (stack)",
 // Summary).  Definition and argument contract: include/moe_gemm1.h.
 //
-// A workgroup (4 waves) computes a BM x 128 tile of y.  BM divides the padding
-// block, so the tile's rows all belong to one expert: expert_of_block gives
-// the weight matrix, sorted_ids gives the token of each row (a padding row
-// stores zeros into LDS and so produces zeros).  The K loop steps by 64: every thread fetches
-// its 16-byte chunks of the next x and W tiles into registers while the waves
-// run v_mfma_f32_32x32x16_bf16 on the current LDS tiles, then stores them into
-// the other LDS buffer (one barrier per step).  LDS rows are XOR-swizzled by
+// A workgroup (4 or 8 waves) computes a BM x BN tile of y (BN = 128 or 256).
+// BM divides the padding block, so the tile's rows all belong to one expert:
+// expert_of_block gives the weight matrix, sorted_ids gives the token of each
+// row (a padding row stores zeros into LDS and so produces zeros).  The K loop
+// steps by 64: every thread fetches its 16-byte chunks of the next x and W
+// tiles into registers while the waves run v_mfma_f32_32x32x16_bf16 on the
+// current LDS tiles, then stores them into the other LDS buffer (one barrier
+// per step).  LDS rows are XOR-swizzled by
 // 16-byte chunk (swz below).  The column tiles of one row tile run back to
 // back on one XCD (tile_of below), so its gathered rows of x are fetched into
 // that XCD's L2 once.  num_post_pad is read on the device: tiles past it
@@ -29,10 +30,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBN = 128;                  // columns of y per workgroup
 constexpr int kBK = 64;                   // K per pipeline step
 constexpr int kChunks = kBK / 8;          // 16-byte chunks per tile row
-constexpr int kThreads = 256;             // 4 waves
 
 struct GArgs {
   const uint16_t* x;
@@ -74,24 +73,28 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <int BM>
-__global__ __launch_bounds__(kThreads) void k_gemm1(GArgs g) {
+// A BM x BN tile per workgroup of BN / 32 waves (each wave 64 x 64 when
+// BM >= 64): the 256-column tile halves the x traffic per MFMA.
+template <int BM, int BN>
+__global__ __launch_bounds__(BN * 2) void k_gemm1(GArgs g) {
+  constexpr int kThreads = BN * 2;
+  constexpr int NW = kThreads / 64;
   constexpr int WGM = BM >= 64 ? 2 : 1;   // waves along the rows
-  constexpr int WGN = 4 / WGM;            // waves along the columns
-  constexpr int WTM = BM / WGM, WTN = kBN / WGN;
+  constexpr int WGN = NW / WGM;           // waves along the columns
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
   constexpr int AP = BM * kChunks / kThreads;  // x chunks per thread per step
-  constexpr int BP = kBN * kChunks / kThreads; // W chunks per thread per step
-  static_assert(AP >= 1 && BP >= 1, "tile too small for the workgroup");
+  constexpr int BP = BN * kChunks / kThreads;  // W chunks per thread per step
+  static_assert(AP >= 1 && BP >= 1 && FM >= 1 && FN >= 1, "tile too small for the workgroup");
   __shared__ u32x4 As[2][BM * kChunks];
-  __shared__ u32x4 Bs[2][kBN * kChunks];
+  __shared__ u32x4 Bs[2][BN * kChunks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   int rt, ct;
-  if (!tile_of((int)blockIdx.x, g.N / kBN, g.nrt, rt, ct)) return;
+  if (!tile_of((int)blockIdx.x, g.N / BN, g.nrt, rt, ct)) return;
   const int r0 = rt * BM;
-  const int n0 = ct * kBN;
+  const int n0 = ct * BN;
   const int npp = min(*g.npp, g.row_limit);
   if (r0 + BM > npp) return;  // npp is a multiple of block and BM divides block
   const int e = g.eob[r0 / g.block];
@@ -196,7 +199,7 @@ int gemm1_impl(const void* x, const void* w, const int32_t* sorted_ids, const in
                const int32_t* num_post_pad, int M, int k, int E, int K, int N, int block, void* y,
                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (M < 0 || k < 1 || k > 64 || E < 1 || E > 4096 || K <= 0 || K % kBK != 0 || N <= 0 ||
-      N % kBN != 0 || block < 32 || block % 32 != 0)
+      N % 128 != 0 || block < 32 || block % 32 != 0)
     return MRS_ERR_INVALID_ARG;
   if (!x || !w || !sorted_ids || !expert_of_block || !num_post_pad || !y) return MRS_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return MRS_ERR_MISALIGNED;
@@ -205,21 +208,24 @@ int gemm1_impl(const void* x, const void* w, const int32_t* sorted_ids, const in
   const int64_t row_limit = max_rows / block * block;
   if (row_limit == 0) return MRS_OK;  // no token: nothing to write
   const int bm = block % 128 == 0 ? 128 : (block % 64 == 0 ? 64 : 32);
-  const int64_t nrt = row_limit / bm, ntn = N / kBN;
+  const int bn = (bm >= 64 && N % 256 == 0) ? 256 : 128;
+  const int64_t nrt = row_limit / bm, ntn = N / bn;
   const int64_t groups = (nrt + kXcds - 1) / kXcds;
   if (groups * kXcds * ntn > INT32_MAX) return MRS_ERR_OVERFLOW;
   GArgs g{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), sorted_ids, expert_of_block,
           num_post_pad, static_cast<uint16_t*>(y), M, k, E, K, N, block, (int)row_limit, (int)nrt};
-  const void* fn = bm == 128 ? reinterpret_cast<const void*>(k_gemm1<128>)
-                   : bm == 64 ? reinterpret_cast<const void*>(k_gemm1<64>)
-                              : reinterpret_cast<const void*>(k_gemm1<32>);
+  const void* fn = bm == 128 ? (bn == 256 ? reinterpret_cast<const void*>(k_gemm1<128, 256>)
+                                          : reinterpret_cast<const void*>(k_gemm1<128, 128>))
+                   : bm == 64 ? (bn == 256 ? reinterpret_cast<const void*>(k_gemm1<64, 256>)
+                                           : reinterpret_cast<const void*>(k_gemm1<64, 128>))
+                              : reinterpret_cast<const void*>(k_gemm1<32, 128>);
   const dim3 grid((unsigned)(groups * kXcds * ntn));
   void* params[] = {&g};
   hipError_t err;
   if (ev0 && ev1)
-    err = hipExtLaunchKernel(fn, grid, dim3(kThreads), params, 0, stream, ev0, ev1, 0);
+    err = hipExtLaunchKernel(fn, grid, dim3(bn * 2), params, 0, stream, ev0, ev1, 0);
   else
-    err = hipLaunchKernel(fn, grid, dim3(kThreads), params, 0, stream);
+    err = hipLaunchKernel(fn, grid, dim3(bn * 2), params, 0, stream);
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 
