@@ -61,6 +61,8 @@ SHAPES = [  # M, E, k, K, N, block
     (1, 32, 16, 3584, 768, 32),
     (513, 64, 8, 512, 384, 128),
     (97, 40, 5, 64, 128, 96),
+    (150, 12, 4, 64, 512, 64),     # one K step; 64 x 256 tiles
+    (90, 20, 3, 128, 256, 256),    # two 128-row tiles per padding block
 ]
 
 
