@@ -175,3 +175,42 @@ def test_full_size_prefill_sampled_rows():
     absp = og.abs_products(xb, wsub, ref.sorted_ids, eobm, M, k, block, rows)
     got = og.bf16_to_f64(y[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16))
     assert np.all(np.abs(got - exact) <= og.tolerance(exact, absp, K))
+
+
+def test_route_sort_and_gemm_in_one_graph_with_changed_inputs():
+    # the handoff needs no host round trip: route-sort and the GEMM captured in
+    # one HIP graph, replayed with new logits and hidden states each time
+    M, E, k, ng, tg, block, K, N = 300, 896, 16, 8, 4, 64, 128, 256
+    cfg = workloads.custom(M, E, k, ng, tg, block, "bf16", "log_zipf", seed=11)
+    sets = [workloads.make_inputs(cfg, seed=s) for s in range(3)]
+    rng = np.random.default_rng(12)
+    xbs = [workloads.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)) for _ in range(3)]
+    wb = workloads.f32_to_bf16_bits(rng.standard_normal((E, N, K)).astype(np.float32) * 0.08)
+    logits = torch.from_numpy(sets[0].logits_storage.view(np.int16)).view(torch.bfloat16).cuda()
+    bias = torch.from_numpy(sets[0].bias).cuda()
+    xg = bits_to_bf16(xbs[0]).cuda()
+    wg = bits_to_bf16(wb).cuda()
+    out = amr.route_sort(logits, bias, k, ng, tg, block)
+    y = amr.grouped_gemm1(xg, wg, out.sorted_ids, out.expert_of_block, out.num_post_pad, k, block)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        amr.route_sort(logits, bias, k, ng, tg, block, out=out)
+        amr.grouped_gemm1(xg, wg, out.sorted_ids, out.expert_of_block, out.num_post_pad, k, block, out=y)
+    for rep in range(6):
+        inp, xb = sets[rep % 3], xbs[rep % 3]
+        logits.copy_(torch.from_numpy(inp.logits_storage.view(np.int16)).view(torch.bfloat16).cuda())
+        bias.copy_(torch.from_numpy(inp.bias).cuda())
+        xg.copy_(bits_to_bf16(xb).cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = orc.route_sort(inp.logits_storage, cfg.dtype, inp.bias, k, ng, tg, block).meta
+        npp = int(out.num_post_pad.item())
+        assert npp == ref.num_post_pad
+        rows = np.arange(npp)
+        exact = og.gemm1_rows(xb, wb, ref.sorted_ids, ref.expert_of_block, M, k, block, rows)
+        absp = og.abs_products(xb, wb, ref.sorted_ids, ref.expert_of_block, M, k, block, rows)
+        got = og.bf16_to_f64(y[:npp].view(torch.int16).cpu().numpy().view(np.uint16))
+        assert np.all(np.abs(got - exact) <= og.tolerance(exact, absp, K)), rep
