@@ -76,7 +76,7 @@ def to_gpu(inp, torch):
     return x, torch.from_numpy(inp.bias).cuda()
 
 
-def graph_size(steps, cap=64):
+def graph_size(steps, cap=25):
     """Calls per captured graph: the largest divisor of `steps` not above `cap`."""
     return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
 
@@ -105,14 +105,17 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
         for _ in range(max(1, warmup // G)):
             graph.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+    # events between the replays split the timed steps into samples of G calls
+    nrep = steps // G
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+    marks[0].record(stream)
     with torch.cuda.stream(stream):
-        for _ in range(steps // G):
+        for i in range(nrep):
             graph.replay()
-    end.record(stream)
+            marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms = marks[0].elapsed_time(marks[-1]) / (nrep * G)
+    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) / G for i in range(nrep)]) * 1e3  # us
     npp = int(out.num_post_pad.item())
     # host wall time per call, launch + synchronise (latency view)
     t = time.perf_counter()
@@ -123,7 +126,9 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     wall_us = (time.perf_counter() - t) / reps * 1e6
     nbytes = algorithmic_bytes(cfg, npp)
     r = dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
-             routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9)
+             routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9,
+             samples=nrep, calls_per_sample=G,
+             us_per_call_p10_p50_p90=[round(float(v), 3) for v in np.percentile(per_call, [10, 50, 90])])
     if per_kernel:
         # HIP events stamped with each kernel's own start and end by the
         # library's launches (hipExtLaunchKernel), same rotation of inputs
@@ -374,6 +379,7 @@ def main():
             c = workloads.CONFIGS[name]
             e = time_workload(c, max(20, args.steps // 4), 5, args.rotate_mb, torch, amr)
             extra[name] = dict(us_per_call=round(e["ms"] * 1e3, 3),
+                               us_per_call_p10_p50_p90=e["us_per_call_p10_p50_p90"],
                                host_wall_us_per_call=round(e["wall_us"], 2),
                                routes_per_s=e["routes_per_s"], algorithmic_gbps=round(e["gbps"], 1),
                                frac_hbm_peak=round(e["gbps"] / HBM_PEAK_GBPS, 4))
@@ -423,6 +429,8 @@ def main():
                    "topk_group": cfg.topk_group, "block": cfg.block, "logits": cfg.dtype},
         "hbm_gbps_algorithmic": r["gbps"],
         "us_per_call": r["ms"] * 1e3,
+        "us_per_call_p10_p50_p90": r["us_per_call_p10_p50_p90"],
+        "timing": {"graph_calls_per_sample": r["calls_per_sample"], "samples": r["samples"]},
         "decode_us_per_call": extra.get("decode", {}).get("us_per_call"),
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
