@@ -729,6 +729,24 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 #pragma unroll
       for (int i = 0; i < EPLM; ++i)
         if (i < epl) put(i, s32[i]);
+    } else if constexpr (MODE == LOAD_STAGE && EPL > 0 && EPL % 4 == 0) {
+      // the lane run is 8-byte aligned: read all of it, then request every
+      // table entry, then form the keys, so a wave waits for LDS twice rather
+      // than once per pair of logits
+      const uint2* s64 = reinterpret_cast<const uint2*>(stage + e0 * 2);
+      uint2 raw[EPL / 4];
+#pragma unroll
+      for (int j = 0; j < EPL / 4; ++j) raw[j] = s64[j];
+      uint32_t off[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL / 4; ++j) {
+        sig_off2(raw[j].x, off[4 * j], off[4 * j + 1]);
+        sig_off2(raw[j].y, off[4 * j + 2], off[4 * j + 3]);
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) av[i] = sig_lds(off[i]);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) put_key(i, av[i] + bias_of(i));
     } else if constexpr (MODE == LOAD_STAGE) {
       if (EPL > 0 ? (EPL % 2 == 0) : (epl % 2 == 0)) {  // the lane run is 4-byte aligned
         const uint32_t* s32 = reinterpret_cast<const uint32_t*>(stage + e0 * 2);
