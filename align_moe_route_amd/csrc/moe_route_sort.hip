@@ -89,6 +89,8 @@ struct Args {
   int seg;    // lanes per token in the wave path (32 or 64)
   int lg_lpg;  // log2 of the lanes per group in the wave path (seg / n_group)
   int epl;     // experts per lane in the wave path (E / seg)
+  int ilw;     // FP32 vector loads, 64-lane segments: lanes of a block of ilw lanes interleave
+               // their 16-byte vectors (1: every lane owns a contiguous run)
   int nbuf;    // LDS row buffers per segment (2 when a wave takes several rounds)
   int stage_bytes;  // bytes of one staged logits row (0: rows are read straight from HBM)
   int tw;      // tokens per workgroup
@@ -697,6 +699,17 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const int epl = EPL > 0 ? EPL : a.epl;
   const int e0 = ls * epl;
   const size_t row = (size_t)(act ? t : 0) * a.E;
+  // Interleaved ownership (FP32 vector loads, one token per wave): the ilw
+  // lanes of a block (a group, or the whole wave when no group stage runs) own
+  // the block's ilw*epl experts as interleaved 16-byte vectors, lane j of the
+  // block holding vectors j, j + ilw, j + 2 ilw, ...; each load instruction
+  // then reads ilw*16 contiguous bytes per block instead of 16 bytes from 64
+  // separate lines.  Register slot i of the lane holds expert expert_of(i).
+  constexpr bool IL = SEG == 64 && !BF16 && MODE == LOAD_VEC;
+  const int ilw = IL ? a.ilw : 1;
+  const int ilj = ls & (ilw - 1);
+  const int il0 = (ls - ilj) * epl + 4 * ilj;  // expert of slot 0
+  auto expert_of = [&](int i) { return IL ? il0 + 4 * ilw * (i >> 2) + (i & 3) : e0 + i; };
   // lanes of segment 1 (32-lane segments): the upper half of the wave
   const unsigned long long seg1 = NSEG == 1 ? 0ull : 0xFFFFFFFF00000000ull;
 
@@ -763,7 +776,8 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
       constexpr int PER = BF16 ? 8 : 4;  // logits per vector
       static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                       (row + e0) * (BF16 ? 2 : 4));
+                                                       (row + (IL ? il0 : e0)) * (BF16 ? 2 : 4));
+      const int vs = IL ? ilw : 1;  // vectors between a lane's consecutive vectors
       // every load of the lane run is issued before the first use (a load past
       // the run repeats the last vector, which stays inside the row)
       constexpr int NQ = EPLM >= PER ? EPLM / PER : 0;
@@ -776,7 +790,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
 #pragma unroll
-        for (int q = 0; q < QB; ++q) raw[q] = src[min(b * QB + q, nq - 1)];
+        for (int q = 0; q < QB; ++q) raw[q] = src[(size_t)min(b * QB + q, nq - 1) * vs];
 #pragma unroll
         for (int qq = 0; qq < QB; ++qq) {
           const int q = b * QB + qq;
@@ -906,7 +920,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     int slot = incl - mine;
     while (cm) {
       const int i = (int)__builtin_ctzll((unsigned long long)cm);
-      ci[slot++] = e0 + i;
+      ci[slot++] = expert_of(i);
       cm &= cm - 1;
     }
   }
@@ -946,7 +960,17 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 
   // ---- 6. outputs in expert order; weights s / sum(s), the sum in float64 ----
   const unsigned long long sb = __ballot(sel) & (NSEG == 1 ? ~0ull : (seg ? seg1 : ~seg1));
-  const int pos = (int)__popcll(sb & ((1ull << lane) - 1ull));
+  int pos = (int)__popcll(sb & ((1ull << lane) - 1ull));
+  if (IL && ilw > 1) {
+    // candidates were compacted in lane order, which is not expert order here:
+    // a pick's position is the number of picks with a smaller expert id
+    int* sv = reinterpret_cast<int*>(cc);
+    wave_sync_lds();  // every lane has finished reading the composites
+    sv[ls] = sel ? ce : 0x7FFFFFFF;
+    wave_sync_lds();
+    pos = 0;
+    for (int j = 0; j < tmax; ++j) pos += sv[j] < ce ? 1 : 0;
+  }
   const double ssum = seg_sum_d<SEG>(sel ? (double)sf : 0.0);
   // |error| <= 2^-24 (sum to FP32) + 2^-23 (rcp) + 2^-24 (product), relative
   const float rs = __builtin_amdgcn_rcpf((float)ssum);
@@ -1027,19 +1051,33 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   }
   if (a.fast) {
     const int epl = EPL > 0 ? EPL : a.epl;
-    const int e0 = ls * epl;
+    // the expert of register slot i (the ownership lean_token uses)
+    constexpr bool IL = SEG == 64 && !BF16 && MODE == LOAD_VEC;
+    const int ilw = IL ? a.ilw : 1;
+    const int ilj = ls & (ilw - 1);
+    const int il0 = (ls - ilj) * epl + 4 * ilj;
+    auto expert_of = [&](int i) { return IL ? il0 + 4 * ilw * (i >> 2) + (i & 3) : ls * epl + i; };
     float bv[EPLM <= kBiasRegMax ? EPLM : 1];
     float bmax = 0.0f;
     if constexpr (EPLM <= kBiasRegMax) {
 #pragma unroll
       for (int i = 0; i < EPLM; ++i) {
-        bv[i] = i < epl ? L.bias[e0 + i] : 0.0f;
+        bv[i] = i < epl ? L.bias[expert_of(i)] : 0.0f;
         bmax = fmaxf(bmax, fabsf(bv[i]));
       }
     } else {
       // lanes read their biases from a transposed copy: lane runs of 64
       // experts would put every lane of a wave on the same LDS bank
-      for (int e = tid; e < a.E; e += kWG) L.biasT[(e % epl) * SEG + e / epl] = L.bias[e];
+      for (int e = tid; e < a.E; e += kWG) {
+        // slot and lane of expert e: inverse of expert_of
+        int slot = e % epl, ln = e / epl;
+        if (IL && ilw > 1) {
+          const int r = e % (ilw * epl), v = r >> 2;
+          slot = 4 * (v / ilw) + (r & 3);
+          ln = (e - r) / epl + v % ilw;
+        }
+        L.biasT[slot * SEG + ln] = L.bias[e];
+      }
       __syncthreads();
       for (int i = 0; i < epl; ++i) bmax = fmaxf(bmax, fabsf(L.biasT[i * SEG + ls]));
     }
@@ -1772,12 +1810,16 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
       a.seg = seg;
       a.lg_lpg = 31 - __builtin_clz((unsigned)(seg / n_group));
       a.epl = epl;
+      // FP32 vector loads with one token per wave: interleave the vectors of
+      // a group's lanes (of the whole wave when no group stage runs)
+      a.ilw = (seg == 64 && !bf16 && vec_mode(epl, false)) ? (a.gstage ? (1 << a.lg_lpg) : 64) : 1;
       a.stage_bytes = sb;
       a.nbuf = nbuf;
     }
   }
   if (!a.fast) {
     a.epl = 1;
+    a.ilw = 1;
     a.stage_bytes = 0;
     a.nbuf = 1;
   }

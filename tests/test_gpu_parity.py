@@ -142,6 +142,12 @@ SWEEP = [
     (8300, 896, 16, 8, 4, 128, "bf16", "log_zipf"),   # staged rows, two buffers
     (9000, 1024, 8, 32, 8, 64, "bf16", "normal"),     # one lane per group
     (20000, 64, 4, 2, 1, 16, "f32", "normal"),        # three rounds per wave
+    # FP32 vector loads, one token per wave: lanes interleave their 16-byte vectors
+    (300, 1024, 16, 1, 1, 16, "f32", "normal"),       # the whole wave interleaved (no group stage)
+    (500, 2048, 8, 4, 4, 32, "f32", "hot"),           # every group kept: the whole wave interleaved
+    (150, 512, 8, 8, 3, 16, "f32", "shared"),         # the 8 lanes of each group interleaved
+    (200, 1024, 16, 1, 1, 8, "f32", "coarse"),        # interleaved, many exact ties
+    (16, 1024, 16, 1, 1, 32, "f32", "duplicated"),    # one workgroup, interleaved, pairs of equal keys
 ]
 
 
