@@ -304,6 +304,61 @@ def traffic_record(kernel, workload):
     return rec
 
 
+def _pmc_medians(path, counter):
+    """Median per dispatch of one counter, by kernel name, from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: (float(np.median(v)), len(v)) for k, v in vals.items()}
+
+
+def write_traffic_record(fetch_csv, write_csv, workload, calib_mb, commands):
+    """HBM bytes per launch of this workload's kernels from two rocprofv3 PMC
+    runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by
+    what the same counter reads for the plain device copy of calib_mb MB that
+    --calib-copy-mb runs first.  Writes profiles/traffic_<dominant>_<workload>.json
+    (read back by traffic_record while the kernel source keeps its hash) and a
+    markdown table of every kernel."""
+    fetch = _pmc_medians(fetch_csv, "FETCH_SIZE")
+    write = _pmc_medians(write_csv, "WRITE_SIZE")
+    calib = int(calib_mb * 1e6) // 4 * 4
+    copy = max((k for k in fetch if "copyBuffer" in k), key=lambda k: fetch[k][0])
+    fscale = calib / (fetch[copy][0] * 1024)
+    wscale = calib / (write[copy][0] * 1024)
+    src = os.path.join(ROOT, "align_moe_route_amd", "csrc", "moe_route_sort.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    ours = [k for k in fetch if k.startswith(("void (anonymous namespace)::k_", "(anonymous namespace)::k_"))]
+    dom = next(k for k in ours if "k_select" in k or "k_small" in k)
+    name = "k_select" if "k_select" in dom else "k_small"
+    rec = {"kernel": name, "workload": workload, "source_sha256": sha,
+           "fetch_bytes": int(round(fetch[dom][0] * 1024 * fscale)),
+           "write_bytes": int(round(write[dom][0] * 1024 * wscale)),
+           "fetch_scale": fscale, "write_scale": wscale, "commands": commands}
+    out = os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic per launch, {workload} workload", "",
+             "Commands (from the repository root):", ""] + ["    " + c for c in commands] + [
+             "", f"Calibration: a plain device copy of {calib} bytes reads FETCH_SIZE = {fetch[copy][0]:.0f} KiB "
+             f"and WRITE_SIZE = {write[copy][0]:.0f} KiB per dispatch; scale factors {fscale:.3f} x 1024 (fetch) "
+             f"and {wscale:.3f} x 1024 (write).", f"Kernel source sha256: {sha}", "",
+             "| kernel | dispatches | FETCH_SIZE KiB (median) | fetch MB (scaled) | WRITE_SIZE KiB (median) "
+             "| write MB (scaled) |", "|---|---|---|---|---|---|"]
+    for k in ours:
+        fk, n = fetch[k]
+        wk = write.get(k, (0.0, 0))[0]
+        lines.append(f"| {k.replace('(anonymous namespace)::', '').split('((')[0]} | {n} | {fk:.0f} | "
+                     f"{fk * 1024 * fscale / 1e6:.3f} | {wk:.0f} | {wk * 1024 * wscale / 1e6:.3f} |")
+    md = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out, md
+
+
 def cpu_baseline(cfg, budget_s=12.0, chunk=1024):
     """The oracle as it stands, on the same workload: one oracle call per chunk
     of tokens, cycling through the workload's tokens until the time budget is
@@ -337,7 +392,19 @@ def main():
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
                     help="first run a plain device-to-device copy of this many MB three times "
                          "(reference dispatches for scaling PMC byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv "
+                         "files of this workload (made with --calib-copy-mb) into profiles/traffic_*")
     args = ap.parse_args()
+    if args.write_traffic:
+        base = (f"python3 bench.py --workload {args.workload} --no-extra --no-cpu-baseline --steps 5 "
+                f"--warmup 1 --calib-copy-mb {args.calib_copy_mb:g}")
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- {base}"
+                for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+        for path in write_traffic_record(args.write_traffic[0], args.write_traffic[1], args.workload,
+                                         args.calib_copy_mb, cmds):
+            print(path)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the route-sort path has no cross-GPU step "
