@@ -1160,6 +1160,47 @@ __device__ int expert_offsets(const Args& a, const Lds& L, int n, F padded) {
   return L.misc[1];
 }
 
+// Single-workgroup kernels: the sentinel rows after each expert's routes and
+// its expert_of_block entries, for experts [0, n) with counts cnt(e) and
+// offsets off[e] (multiples of the block).  A wave whose experts have short
+// runs of sentinel rows lets every lane write its own expert's rows (one store
+// per row of the longest run); when the longest run is more than four times
+// the number of its experts with routes (a step of the walk costs about four
+// such stores), the wave walks those experts and its 64 lanes write one
+// expert's rows together.
+template <typename F>
+__device__ void write_padding(const Args& a, int n, const int* off, F cnt) {
+  const int lane = lane_id();
+  const int sentinel = a.M * a.k;
+  for (int eb = (int)threadIdx.x - lane; eb < n; eb += kWG) {  // wave-uniform base
+    const int e = eb + lane;
+    int c = 0, p = 0, o = 0;
+    if (e < n) {
+      c = cnt(e);
+      p = pad_block(c, a);
+      o = off[e];
+    }
+    unsigned long long m = __ballot(p > 0);
+    if (!m) continue;
+    if ((int)wave_max_u32((uint32_t)(p - c)) <= 4 * (int)__popcll(m)) {
+      if (p > 0) {
+        for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
+        for (int b = div_block(o, a); b < div_block(o + p, a); ++b) a.eob[b] = e;
+      }
+      continue;
+    }
+    while (m) {
+      const int l = (int)__builtin_ctzll(m);
+      m &= m - 1;
+      const int cl = (int)readlane((uint32_t)c, l), pl = (int)readlane((uint32_t)p, l);
+      const int ol = (int)readlane((uint32_t)o, l);
+      for (int r = cl + lane; r < pl; r += kWave) a.sorted_ids[ol + r] = sentinel;
+      const int b0 = div_block(ol, a), nb = div_block(pl, a);
+      for (int b = lane; b < nb; b += kWave) a.eob[b0 + b] = eb + l;
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Kernels.
 // ----------------------------------------------------------------------------
@@ -1174,13 +1215,7 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const int total = expert_offsets(a, L, a.EL, [&](int e) { return pad_block(__popcll(bits[e]), a); });
   if (tid == 0) *a.npp = total;
   const int sentinel = a.M * a.k;
-  for (int e = tid; e < a.EL; e += kWG) {
-    const int c = __popcll(bits[e]);
-    const int p = pad_block(c, a);
-    const int o = L.off[e];
-    for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
-    for (int b = div_block(o, a); b < div_block(o + p, a); ++b) a.eob[b] = e;
-  }
+  write_padding(a, a.EL, L.off, [&](int e) { return __popcll(bits[e]); });
   for (int q = tid; q < sentinel; q += kWG) {
     const int tl = q / a.k;
     const int e = L.ids[q] - a.e_lo;
@@ -1484,13 +1519,7 @@ __global__ __launch_bounds__(kWG) void k_ids_small(Args a) {
   if (tid == kWG - 1) *a.npp = pre;
   __syncthreads();
   const int sentinel = a.M * a.k;
-  for (int e = tid; e < a.E; e += kWG) {
-    const int c = L.cnt[e];
-    const int p = pad_block(c, a);
-    const int o = L.off[e];
-    for (int r = c; r < p; ++r) a.sorted_ids[o + r] = sentinel;
-    for (int b = div_block(o, a); b < div_block(o + p, a); ++b) a.eob[b] = e;
-  }
+  write_padding(a, a.E, L.off, [&](int e) { return L.cnt[e]; });
   for (int q = tid; q < sentinel; q += kWG) {
     const int r = L.rec[q];
     if (r >= 0) a.sorted_ids[L.off[r & 0xFFFF] + (r >> 16)] = q;
