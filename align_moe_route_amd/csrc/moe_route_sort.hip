@@ -563,6 +563,29 @@ __device__ void exact_token_wg(const Args& a, const Lds& L, int t, int tl, int* 
 // owns experts [l*epl, (l+1)*epl) with epl = E / SEG.  EPL > 0 fixes epl at
 // compile time; EPL == 0 reads it from the arguments (up to 64).
 // ----------------------------------------------------------------------------
+// Which experts a lane of a wave-path segment holds in its register slots.
+// Contiguous runs (w = 1): slot i of lane l holds expert l*epl + i.
+// Interleaved (w > 1; FP32 vector loads, one token per wave): the w lanes of a
+// block (a group, or the whole wave when no group stage runs) hold the
+// block's w*epl experts as interleaved 16-byte vectors, lane j of the block
+// holding vectors j, j + w, j + 2w, ..., so one load instruction reads w*16
+// contiguous bytes per block instead of 16 bytes from each of 64 separate
+// lines.  Every lane still holds experts of one group only.
+struct Ownership {
+  int w, e_slot0;  // block width in lanes, expert of slot 0
+  __device__ __forceinline__ Ownership(int ls, int epl, int w_) : w(w_) {
+    const int j = ls & (w - 1);
+    e_slot0 = (ls - j) * epl + 4 * j;
+  }
+  __device__ __forceinline__ int expert(int i) const { return e_slot0 + 4 * w * (i >> 2) + (i & 3); }
+  // slot and lane of expert e: the inverse of expert()
+  __device__ static void place(int e, int epl, int w, int& slot, int& lane) {
+    const int r = e % (w * epl), v = r >> 2;
+    slot = 4 * (v / w) + (r & 3);
+    lane = (e - r) / epl + v % w;
+  }
+};
+
 // s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N), N < 64
@@ -699,17 +722,10 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const int epl = EPL > 0 ? EPL : a.epl;
   const int e0 = ls * epl;
   const size_t row = (size_t)(act ? t : 0) * a.E;
-  // Interleaved ownership (FP32 vector loads, one token per wave): the ilw
-  // lanes of a block (a group, or the whole wave when no group stage runs) own
-  // the block's ilw*epl experts as interleaved 16-byte vectors, lane j of the
-  // block holding vectors j, j + ilw, j + 2 ilw, ...; each load instruction
-  // then reads ilw*16 contiguous bytes per block instead of 16 bytes from 64
-  // separate lines.  Register slot i of the lane holds expert expert_of(i).
+  // register slot i of the lane holds expert own.expert(i) (see Ownership)
   constexpr bool IL = SEG == 64 && !BF16 && MODE == LOAD_VEC;
   const int ilw = IL ? a.ilw : 1;
-  const int ilj = ls & (ilw - 1);
-  const int il0 = (ls - ilj) * epl + 4 * ilj;  // expert of slot 0
-  auto expert_of = [&](int i) { return IL ? il0 + 4 * ilw * (i >> 2) + (i & 3) : e0 + i; };
+  const Ownership own(ls, epl, ilw);
   // lanes of segment 1 (32-lane segments): the upper half of the wave
   const unsigned long long seg1 = NSEG == 1 ? 0ull : 0xFFFFFFFF00000000ull;
 
@@ -776,7 +792,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
       constexpr int PER = BF16 ? 8 : 4;  // logits per vector
       static_assert(EPLM < PER || EPLM % PER == 0, "vector width");
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.logits) +
-                                                       (row + (IL ? il0 : e0)) * (BF16 ? 2 : 4));
+                                                       (row + own.e_slot0) * (BF16 ? 2 : 4));
       const int vs = IL ? ilw : 1;  // vectors between a lane's consecutive vectors
       // every load of the lane run is issued before the first use (a load past
       // the run repeats the last vector, which stays inside the row)
@@ -920,7 +936,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     int slot = incl - mine;
     while (cm) {
       const int i = (int)__builtin_ctzll((unsigned long long)cm);
-      ci[slot++] = expert_of(i);
+      ci[slot++] = own.expert(i);
       cm &= cm - 1;
     }
   }
@@ -1053,31 +1069,24 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   }
   if (a.fast) {
     const int epl = EPL > 0 ? EPL : a.epl;
-    // the expert of register slot i (the ownership lean_token uses)
+    // the experts of the lane's register slots, as lean_token holds them
     constexpr bool IL = SEG == 64 && !BF16 && MODE == LOAD_VEC;
     const int ilw = IL ? a.ilw : 1;
-    const int ilj = ls & (ilw - 1);
-    const int il0 = (ls - ilj) * epl + 4 * ilj;
-    auto expert_of = [&](int i) { return IL ? il0 + 4 * ilw * (i >> 2) + (i & 3) : ls * epl + i; };
+    const Ownership own(ls, epl, ilw);
     float bv[EPLM <= kBiasRegMax ? EPLM : 1];
     float bmax = 0.0f;
     if constexpr (EPLM <= kBiasRegMax) {
 #pragma unroll
       for (int i = 0; i < EPLM; ++i) {
-        bv[i] = i < epl ? L.bias[expert_of(i)] : 0.0f;
+        bv[i] = i < epl ? L.bias[own.expert(i)] : 0.0f;
         bmax = fmaxf(bmax, fabsf(bv[i]));
       }
     } else {
       // lanes read their biases from a transposed copy: lane runs of 64
       // experts would put every lane of a wave on the same LDS bank
       for (int e = tid; e < a.E; e += kWG) {
-        // slot and lane of expert e: inverse of expert_of
-        int slot = e % epl, ln = e / epl;
-        if (IL && ilw > 1) {
-          const int r = e % (ilw * epl), v = r >> 2;
-          slot = 4 * (v / ilw) + (r & 3);
-          ln = (e - r) / epl + v % ilw;
-        }
+        int slot, ln;
+        Ownership::place(e, epl, ilw, slot, ln);
         L.biasT[slot * SEG + ln] = L.bias[e];
       }
       __syncthreads();
