@@ -148,6 +148,8 @@ SWEEP = [
     (150, 512, 8, 8, 3, 16, "f32", "shared"),         # the 8 lanes of each group interleaved
     (200, 1024, 16, 1, 1, 8, "f32", "coarse"),        # interleaved, many exact ties
     (16, 1024, 16, 1, 1, 32, "f32", "duplicated"),    # one workgroup, interleaved, pairs of equal keys
+    (120, 1280, 16, 4, 2, 64, "f32", "normal"),       # 20 experts per lane (5 vectors), 16-lane blocks
+    (90, 768, 8, 8, 3, 16, "f32", "hot"),             # 12 experts per lane (3 vectors), 8-lane blocks
 ]
 
 
