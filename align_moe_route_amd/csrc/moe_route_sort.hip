@@ -12,7 +12,8 @@
 // compute overlaps the others' copies) or read as 16-byte vectors.
 //
 // Selection, one token per wave segment of 32 or 64 lanes; lane l owns
-// experts [l*epl, (l+1)*epl):
+// experts [l*epl, (l+1)*epl), or, for FP32 rows read as 16-byte vectors with
+// one token per wave, interleaved vectors of its group (see Ownership):
 //   1. keys = sigmoid(x) + b and each lane's two largest keys.  BF16 logits
 //      look their sigmoid up in an LDS table that is correctly rounded for
 //      every BF16 value, so the keys are exact.  FP32 logits use sigmoid_fast
