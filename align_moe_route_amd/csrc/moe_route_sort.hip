@@ -1220,6 +1220,19 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
   select_tokens<SEG, EPL, BF16, MODE>(a, L, 0, a.M);
   const int tid = threadIdx.x;
+  if (a.M == 1 && a.e_lo == 0 && a.EL == a.E) {
+    // one token over all experts: its k picks are distinct and ascending, so
+    // pick j owns rows [j*block, (j+1)*block) -- its slot j, then sentinels
+    // (M*k = k) -- and block j; no scan over the experts is needed
+    const int rows = a.k * a.block;
+    for (int r = tid; r < rows; r += kWG) {
+      const int j = div_block(r, a);
+      a.sorted_ids[r] = r == j * a.block ? j : a.k;
+    }
+    for (int j = tid; j < a.k; j += kWG) a.eob[j] = L.ids[j];
+    if (tid == 0) *a.npp = rows;
+    return;
+  }
   // metadata of experts [e_lo, e_lo + EL), numbered from 0
   const unsigned long long* bits = L.bits + a.e_lo;
   const int total = expert_offsets(a, L, a.EL, [&](int e) { return pad_block(__popcll(bits[e]), a); });
