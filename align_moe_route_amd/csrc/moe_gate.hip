@@ -116,7 +116,9 @@ extern "C" int moe_gate_route_sort(const void* hidden, const void* w_gate, const
         hipSuccess)
       return MRS_ERR_LAUNCH;
   }
-  // M <= 64: the route-sort runs in one workgroup and needs no workspace
-  return moe_route_sort(out_logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
-                        expert_of_block, num_post_pad, MRS_DTYPE_F32, nullptr, 0, stream);
+  // M <= 64: the route-sort runs in one workgroup (asked for explicitly), so it
+  // needs no workspace
+  return moe_route_sort_ex(out_logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w, sorted_ids,
+                           expert_of_block, num_post_pad, MRS_DTYPE_F32, nullptr, 0, stream,
+                           MRS_FLAG_FORCE_SINGLE_WG, nullptr);
 }

@@ -1589,6 +1589,17 @@ __global__ __launch_bounds__(256) void k_sigmoid_table_probe(const uint16_t* h, 
 // ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
+// One workgroup for the whole call (one launch) while that is faster than
+// the three-launch path: its time grows with M and E while the other stays
+// near 12-25 us.  Measured crossovers (one workgroup faster below them): 56
+// tokens at E = 64 (FP32), 28 at E = 896 (BF16), 20 at E = 4096 (FP32), which
+// M^4 * E = 6.3e8 follows; up to 16 tokens (one per wave) it was faster at
+// every E measured.
+bool single_wg_faster(int M, int E) {
+  const double m = M;
+  return M <= 16 || m * m * m * m * E <= 6.3e8;
+}
+
 int choose_tw(int M) {
   int tw = (M + 255) / 256;  // one workgroup per compute unit
   // at least 4 tokens per workgroup: below that, the per-workgroup copies of
@@ -1842,7 +1853,8 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   a.stats = stats;
   const bool bf16 = logits_dtype == MRS_DTYPE_BF16;
   const int sz = bf16 ? 2 : 4;
-  const bool want_small = M <= kTwMax && !(flags & MRS_FLAG_FORCE_MULTI_WG);
+  const bool want_small = M <= kTwMax && !(flags & MRS_FLAG_FORCE_MULTI_WG) &&
+                          ((flags & MRS_FLAG_FORCE_SINGLE_WG) || single_wg_faster(M, E));
   const int tw = want_small ? M : choose_tw(M);
 
   // Wave layout: 32-lane segments (two tokens per wave) when the shape allows

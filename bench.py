@@ -490,6 +490,14 @@ def main():
                 f"{e['gbps']:.1f} GB/s")
 
     if not args.no_extra:
+        # batched decode on the decode shape (896 experts, top-16, 8 groups keep 4,
+        # block 32, BF16): the batch sizes where the one-workgroup and the
+        # three-launch paths trade places
+        for mb in (32, 64):
+            c = workloads.custom(mb, 896, 16, 8, 4, 32, "bf16", "normal", seed=0, name=f"decode_batch_{mb}")
+            e = time_workload(c, max(20, args.steps // 4), 5, args.rotate_mb, torch, amr)
+            extra[c.name] = dict(us_per_call=round(e["ms"] * 1e3, 3), routes_per_s=e["routes_per_s"])
+            log(f"[bench] {c.name}: {e['ms']*1e3:.2f} us/call")
         so = time_sort_from_ids(cfg, max(20, args.steps // 4), torch, amr)
         extra["sort_from_ids_" + cfg.name] = so
         log(f"[bench] sort_from_ids on {cfg.name} ids: {so['us_per_call']:.2f} us/call, "

@@ -161,6 +161,17 @@ def test_sweep_parity(case):
     assert_parity(inp, run(inp))
 
 
+# the single-workgroup path on every small sweep shape, whichever path the
+# library would pick for it
+@pytest.mark.parametrize("case", [c for c in SWEEP if c[0] <= 64],
+                         ids=lambda c: "M{}_E{}_k{}_g{}-{}_b{}_{}_{}".format(*c))
+def test_sweep_parity_single_workgroup(case):
+    M, E, k, ng, tg, block, dtype, dist = case
+    cfg = workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=M + E)
+    inp = workloads.make_inputs(cfg)
+    assert_parity(inp, run(inp, flags=amr.FLAG_FORCE_SINGLE_WG))
+
+
 @pytest.mark.parametrize("dist", ["normal", "hot", "shared", "dominant_group", "log_zipf", "equal",
                                   "duplicated", "coarse"])
 def test_distributions_prefill_shape(dist):
