@@ -110,6 +110,8 @@ struct Args {
   int32_t* ws_pad;   // [E] padded routes per expert
   int32_t* ws_hist;  // [nwg][E] per-workgroup counts, then exclusive column prefixes
   int32_t* ws_slot;  // [M*k] expert | (rank inside the workgroup << 16)
+  int fold;          // at most kFoldRows workgroups: the scatter sums the raw histogram rows
+                     // itself and the column-scan launch is skipped
   int32_t* stats;
   const int32_t* in_ids;  // sort-only entry: caller's expert ids [M, k]
   int e_lo, EL;  // experts [e_lo, e_lo + EL) get metadata (all E unless a local range is asked for)
@@ -1339,6 +1341,10 @@ __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
 // it writes) is requested up front, so the block waits for one round trip.
 constexpr int kRecPerThread = (kTwMax * 64 + kWG - 1) / kWG;
 constexpr int kEPerThread = kEMax / kWG;
+// With this many workgroups or fewer, each scatter block reads every raw
+// histogram row itself (one load per row and expert, all in flight together)
+// instead of waiting for a column-scan launch.
+constexpr int kFoldRows = 16;
 
 __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   const Lds L = carve(KIND_SCATTER, a);
@@ -1352,26 +1358,56 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   const int ept = (a.E + kWG - 1) / kWG;  // experts per thread in the offset scan (contiguous)
   const int es0 = (int)((int64_t)w * a.E / a.nwg);
   const int es1 = (int)((int64_t)(w + 1) * a.E / a.nwg);
-  int rv[kRecPerThread], pv[kEPerThread], cv[kEPerThread], tv[kEPerThread];
+  int rv[kRecPerThread], pv[kEPerThread];
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
     const int q = tid + j * kWG;
     rv[j] = q < ns ? rec[q] : 0;
   }
-#pragma unroll
-  for (int i = 0; i < kEPerThread; ++i) {
-    const int e = tid * ept + i;
-    pv[i] = (i < ept && e < a.E) ? a.ws_pad[e] : 0;
-    const int e2 = tid + i * kWG;
-    cv[i] = e2 < a.E ? colpre[e2] : 0;
-    tv[i] = es0 + e2 < es1 ? a.ws_tot[es0 + e2] : 0;  // counts of the experts this block pads
-  }
+  // cnt: counts of the experts this block pads (at e - es0), or, folded, of
+  // every expert (at e)
   int* cnt = L.cpre + a.E;
+  if (a.fold) {
+    // the column prefix of this block (rows before it) and every expert's
+    // total, from the raw histogram rows
+#pragma unroll 1
+    for (int i = 0; i < kEPerThread; ++i) {
+      const int e2 = tid + i * kWG;
+      if (e2 >= a.E) break;
+      int hv[kFoldRows];
 #pragma unroll
-  for (int i = 0; i < kEPerThread; ++i) {
-    const int e2 = tid + i * kWG;
-    if (e2 < a.E) L.cpre[e2] = cv[i];
-    if (es0 + e2 < es1) cnt[e2] = tv[i];
+      for (int r = 0; r < kFoldRows; ++r) hv[r] = r < a.nwg ? a.ws_hist[(size_t)r * a.E + e2] : 0;
+      int tot = 0, pre = 0;
+#pragma unroll
+      for (int r = 0; r < kFoldRows; ++r) {
+        tot += hv[r];
+        pre += r < w ? hv[r] : 0;
+      }
+      L.cpre[e2] = pre;
+      cnt[e2] = tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kEPerThread; ++i) {
+      const int e = tid * ept + i;
+      pv[i] = (i < ept && e < a.E) ? pad_block(cnt[e], a) : 0;
+    }
+  } else {
+    int cv[kEPerThread], tv[kEPerThread];
+#pragma unroll
+    for (int i = 0; i < kEPerThread; ++i) {
+      const int e = tid * ept + i;
+      pv[i] = (i < ept && e < a.E) ? a.ws_pad[e] : 0;
+      const int e2 = tid + i * kWG;
+      cv[i] = e2 < a.E ? colpre[e2] : 0;
+      tv[i] = es0 + e2 < es1 ? a.ws_tot[es0 + e2] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kEPerThread; ++i) {
+      const int e2 = tid + i * kWG;
+      if (e2 < a.E) L.cpre[e2] = cv[i];
+      if (es0 + e2 < es1) cnt[e2] = tv[i];
+    }
   }
   // exclusive scan of the padded totals over all experts
   int local = 0;
@@ -1394,7 +1430,7 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   // one wave per expert of this block's share: padding rows, expert_of_block
   const int lane = lane_id();
   for (int e = es0 + (tid >> 6); e < es1; e += kNW) {
-    const int c = cnt[e - es0];
+    const int c = cnt[a.fold ? e : e - es0];
     const int o = L.off[e];
     const int p = (e + 1 < a.E ? L.off[e + 1] : total) - o;
     for (int r = c + lane; r < p; r += kWave) a.sorted_ids[o + r] = sentinel;
@@ -1928,6 +1964,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
+  a.fold = a.nwg <= kFoldRows ? 1 : 0;
   const size_t lds_sel = lds_plan(KIND_SELECT, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k, 0).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
@@ -1939,7 +1976,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   Args as = a;
   as.E = EL;
   void* p_sort[] = {&as};
-  if (rc == MRS_OK)
+  if (rc == MRS_OK && !as.fold)
     rc = launch(reinterpret_cast<const void*>(k_colscan), (EL + kWave - 1) / kWave, kWG, 0, st, p_sort, tm);
   if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_sort, tm);
   return rc;
@@ -2044,11 +2081,12 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
+  a.fold = a.nwg <= kFoldRows ? 1 : 0;
   const size_t lds_h = ids_lds_bytes(E, a.tw, k, &oc, &orc, &oo, &om, &osc);
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, 1, 0, 0, a.tw, k, 0).total;
   if (lds_h > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   int rc = launch(reinterpret_cast<const void*>(k_ids_hist), a.nwg, kWG, lds_h, st, p_one, nullptr);
-  if (rc == MRS_OK)
+  if (rc == MRS_OK && !a.fold)
     rc = launch(reinterpret_cast<const void*>(k_colscan), (E + kWave - 1) / kWave, kWG, 0, st, p_one, nullptr);
   if (rc == MRS_OK) rc = launch(reinterpret_cast<const void*>(k_scatter), a.nwg, kWG, lds_sct, st, p_one, nullptr);
   return rc;

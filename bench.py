@@ -57,15 +57,17 @@ def launch_bytes(cfg, npp, launches):
     """Algorithmic bytes attributed to each launch of one call.  One launch:
     everything.  Three launches: selection (logits + bias in, ids + weights
     out), column scan of the workgroup histograms (workspace only), scatter
-    (sorted rows, expert per block, row count)."""
+    (sorted rows, expert per block, row count); two launches (few
+    workgroups): the same without the column scan."""
     if launches == 1:
         return [algorithmic_bytes(cfg, npp)]
     sz = 2 if cfg.dtype == "bf16" else 4
-    return [cfg.M * cfg.E * sz + 4 * cfg.E + 8 * cfg.M * cfg.k, 0,
-            4 * npp + 4 * (npp // cfg.block) + 4]
+    sel = cfg.M * cfg.E * sz + 4 * cfg.E + 8 * cfg.M * cfg.k
+    sct = 4 * npp + 4 * (npp // cfg.block) + 4
+    return [sel, sct] if launches == 2 else [sel, 0, sct]
 
 
-KERNELS = {1: ["k_small"], 3: ["k_select", "k_colscan", "k_scatter"]}
+KERNELS = {1: ["k_small"], 2: ["k_select", "k_scatter"], 3: ["k_select", "k_colscan", "k_scatter"]}
 
 
 def to_gpu(inp, torch):
