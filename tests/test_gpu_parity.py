@@ -150,6 +150,11 @@ SWEEP = [
     (16, 1024, 16, 1, 1, 32, "f32", "duplicated"),    # one workgroup, interleaved, pairs of equal keys
     (120, 1280, 16, 4, 2, 64, "f32", "normal"),       # 20 experts per lane (5 vectors), 16-lane blocks
     (90, 768, 8, 8, 3, 16, "f32", "hot"),             # 12 experts per lane (3 vectors), 8-lane blocks
+    # 64 experts per lane: blocks of two groups (the two load batches)
+    (85, 4096, 16, 4, 2, 64, "f32", "normal"),        # 16-lane groups, 32-lane blocks
+    (90, 4096, 16, 8, 3, 64, "f32", "hot"),           # 8-lane groups, 16-lane blocks
+    (75, 4096, 16, 16, 8, 128, "f32", "coarse"),      # 4-lane groups, 8-lane blocks, many exact ties
+    (80, 4096, 8, 32, 10, 32, "f32", "shared"),       # 2-lane groups, 4-lane blocks
 ]
 
 
