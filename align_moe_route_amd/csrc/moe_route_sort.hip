@@ -1335,10 +1335,11 @@ __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
   }
 }
 
-// Launch 3: expert offsets, padding, expert_of_block and the stable scatter.
-// Everything the block reads from the workspace (its slot records, the padded
-// totals, its row of column prefixes, the counts of the experts whose padding
-// it writes) is requested up front, so the block waits for one round trip.
+// Last launch: expert offsets, padding, expert_of_block and the stable
+// scatter.  Everything the block reads from the workspace (its slot records,
+// the padded totals, its row of column prefixes, the counts of the experts
+// whose padding it writes -- or, folded, the raw histogram rows) is requested
+// up front, so the block waits for one round trip.
 constexpr int kRecPerThread = (kTwMax * 64 + kWG - 1) / kWG;
 constexpr int kEPerThread = kEMax / kWG;
 // With this many workgroups or fewer, each scatter block reads every raw
