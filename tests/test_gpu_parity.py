@@ -155,6 +155,15 @@ SWEEP = [
     (90, 4096, 16, 8, 3, 64, "f32", "hot"),           # 8-lane groups, 16-lane blocks
     (75, 4096, 16, 16, 8, 128, "f32", "coarse"),      # 4-lane groups, 8-lane blocks, many exact ties
     (80, 4096, 8, 32, 10, 32, "f32", "shared"),       # 2-lane groups, 4-lane blocks
+    # at the limits of the contract: k = 64 with E = 4096, thousands of groups,
+    # groups of one expert, blocks larger than any expert's count
+    (40, 4096, 64, 1, 1, 1024, "bf16", "normal"),      # one group, 1024-row blocks
+    (3000, 4096, 64, 8, 8, 256, "f32", "hot"),         # every group kept, several workgroups
+    (2, 4096, 64, 64, 64, 1, "f32", "equal"),          # all keys equal, every group kept
+    (700, 896, 64, 8, 8, 4096, "bf16", "log_zipf"),    # block above M: one block per used expert
+    (50, 4096, 64, 2048, 40, 32, "f32", "normal"),     # 2048 groups of two
+    (1, 4096, 64, 4096, 64, 1, "bf16", "coarse"),      # 4096 groups of one
+    (130, 4096, 64, 4096, 100, 16, "f32", "normal"),   # groups of one, several workgroups
 ]
 
 
