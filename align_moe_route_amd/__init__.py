@@ -133,17 +133,29 @@ class RouteSortOutput(NamedTuple):
     num_post_pad: "torch.Tensor"     # [1] int32 (device)
 
 
+# (device, stream handle) -> the workspaces made for that stream, the last the
+# largest.  No call reads workspace words that an earlier call left, so one
+# buffer serves every shape that fits in it.
 _ws_cache = {}
 
 
-def _workspace(device, nbytes: int):
+def _workspace(device, stream_handle: int, nbytes: int):
+    """A zeroed workspace of at least nbytes for calls on one stream.
+
+    Calls on one stream run in order and share a buffer; calls on different
+    streams may overlap in time and each stream gets buffers of its own.  An
+    outgrown buffer is kept, not freed, since a captured graph may still hold
+    its address; sizes are powers of two, so a stream's buffers add up to less
+    than twice the largest."""
     import torch
-    key = (str(device), nbytes)
-    ws = _ws_cache.get(key)
-    if ws is None:
-        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
-    return ws
+    bufs = _ws_cache.setdefault((str(device), int(stream_handle)), [])
+    if bufs and bufs[-1].numel() >= nbytes:
+        return bufs[-1]
+    size = 256
+    while size < nbytes:
+        size *= 2
+    bufs.append(torch.zeros(size, dtype=torch.uint8, device=device))
+    return bufs[-1]
 
 
 def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
@@ -155,7 +167,10 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
     bias:   [E] float32 tensor on the same device.
     out:    optional preallocated RouteSortOutput (reused, nothing else written).
     workspace: optional uint8 tensor of at least workspace_bytes() bytes that
-            was zeroed once; by default a cached per-device buffer is used.
+            was zeroed once; by default a cached buffer of the call's stream
+            (calls on different streams may then overlap in time).  Make the
+            first call on a stream before capturing a graph on it, or the
+            allocation and zero fill of that buffer join the graph.
     stats:  optional int32 [2] device tensor (exact-path / fast-path token counts).
     events: optional list of 6 torch.cuda.Event(enable_timing=True); events
             2i and 2i+1 take the start and end of the call's kernel i (pairs
@@ -210,12 +225,12 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
                 out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
             raise ValueError("out metadata buffers too small or of the wrong dtype")
     nbytes = workspace_bytes(M, E, k, block)
-    if workspace is None:
-        workspace = _workspace(dev, nbytes) if nbytes else None
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream.cuda_stream, nbytes) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if local is not None:
         rc = int(lib().moe_route_sort_local(
             logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block, lb, lc,
@@ -302,12 +317,12 @@ def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, 
           out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
         raise ValueError("out buffers too small or of the wrong dtype")
     nbytes = workspace_bytes(M, E, k, block)
-    if workspace is None:
-        workspace = _workspace(dev, nbytes) if nbytes else None
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream.cuda_stream, nbytes) if nbytes else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
                                      out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), ws_ptr,
                                      ws_len, stream.cuda_stream))

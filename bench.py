@@ -92,12 +92,16 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     # no reuse of cached lines between consecutive steps
     xs = [x0] + [torch.roll(x0, shifts=(i * 997) % max(cfg.M, 1), dims=0).contiguous()
                  for i in range(1, nrot)]
-    out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    # Every call runs on one stream; its first call, outside the capture,
+    # allocates the stream's workspace, so the graph holds route-sort launches
+    # only.
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
     torch.cuda.synchronize()
     # The timed steps replay a HIP graph of G consecutive calls (rotating inputs),
     # so host-side launch overhead does not pace the GPU.
     G = graph_size(steps)
-    stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for i in range(G):
@@ -122,9 +126,10 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     # host wall time per call, launch + synchronise (latency view)
     t = time.perf_counter()
     reps = min(steps, 50)
-    for i in range(reps):
-        amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
-        torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(reps):
+            amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+            torch.cuda.synchronize()
     wall_us = (time.perf_counter() - t) / reps * 1e6
     nbytes = algorithmic_bytes(cfg, npp)
     r = dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
@@ -136,9 +141,10 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
         # library's launches (hipExtLaunchKernel), same rotation of inputs
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
         launches = 0
-        for i in range(steps):
-            _, launches = amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
-                                         out=out, events=evs[i])
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                _, launches = amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
+                                             out=out, events=evs[i])
         torch.cuda.synchronize()
         per = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(launches)]
                         for i in range(steps)]) * 1e3  # us
@@ -153,11 +159,12 @@ def time_sort_from_ids(cfg, steps, torch, amr):
     workload (same skew), timed like the main loop (graph replay)."""
     inp = workloads.make_inputs(cfg)
     x0, b = to_gpu(inp, torch)
-    ids = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block).ids
-    out = amr.sort_from_ids(ids, cfg.E, cfg.block)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # the stream's workspace, allocated outside the capture
+        ids = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block).ids
+        out = amr.sort_from_ids(ids, cfg.E, cfg.block)
     torch.cuda.synchronize()
     G = graph_size(steps)
-    stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for _ in range(G):
@@ -185,10 +192,11 @@ def time_local(cfg, steps, ranks, torch, amr):
     inp = workloads.make_inputs(cfg)
     x0, b = to_gpu(inp, torch)
     rng_ = (0, cfg.E // ranks)
-    out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, local=rng_)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # the stream's workspace, allocated outside the capture
+        out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, local=rng_)
     torch.cuda.synchronize()
     G = graph_size(steps)
-    stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for _ in range(G):

@@ -190,10 +190,11 @@ def test_route_sort_and_gemm_in_one_graph_with_changed_inputs():
     bias = torch.from_numpy(sets[0].bias).cuda()
     xg = bits_to_bf16(xbs[0]).cuda()
     wg = bits_to_bf16(wb).cuda()
-    out = amr.route_sort(logits, bias, k, ng, tg, block)
-    y = amr.grouped_gemm1(xg, wg, out.sorted_ids, out.expert_of_block, out.num_post_pad, k, block)
-    torch.cuda.synchronize()
     stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # the stream's workspace, allocated outside the capture
+        out = amr.route_sort(logits, bias, k, ng, tg, block)
+        y = amr.grouped_gemm1(xg, wg, out.sorted_ids, out.expert_of_block, out.num_post_pad, k, block)
+    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         amr.route_sort(logits, bias, k, ng, tg, block, out=out)

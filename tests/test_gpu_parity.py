@@ -250,9 +250,10 @@ def test_graph_replay_with_changed_inputs():
     cfg = workloads.custom(512, 896, 16, 8, 4, 64, "bf16", "normal", seed=30)
     sets = [workloads.make_inputs(cfg, seed=s) for s in range(4)]
     x, b = to_gpu(sets[0])
-    out = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)  # warm up, allocate
-    torch.cuda.synchronize()
     stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # warm up: outputs and the stream's workspace, outside the capture
+        out = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
@@ -265,6 +266,27 @@ def test_graph_replay_with_changed_inputs():
         graph.replay()
         g = fetch(out, cfg.block)
         assert_parity(inp, g)
+
+
+def test_concurrent_streams_default_workspace():
+    """Calls queued on two streams, free to overlap in time, each with the
+    binding's default workspace (one per stream): both match the oracle."""
+    cfg = workloads.custom(4096, 896, 16, 8, 4, 64, "bf16", "log_zipf", seed=40)
+    inps = [workloads.make_inputs(cfg, seed=s) for s in (40, 41)]
+    dev = [to_gpu(i) for i in inps]
+    outs = [amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block) for x, b in dev]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print(f"[gpu] two streams, M={cfg.M} E={cfg.E} x10 calls each", flush=True)
+    for _ in range(10):
+        for (x, b), out, s in zip(dev, outs, streams):
+            with torch.cuda.stream(s):
+                amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    torch.cuda.synchronize()
+    ws = {amr._ws_cache[(str(x.device), s.cuda_stream)][-1].data_ptr() for (x, _), s in zip(dev, streams)}
+    assert len(ws) == 2
+    for inp, out in zip(inps, outs):
+        assert_parity(inp, fetch(out, cfg.block))
 
 
 def test_stats_count_every_token():

@@ -241,3 +241,25 @@ def test_gate_checks():
         assert gate_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER, name
     for name in ("h", "w", "logits"):
         assert gate_call(**{name: P + 8}) == amr.MRS_ERR_MISALIGNED, name
+
+
+def test_default_workspace_per_stream(monkeypatch):
+    """The binding's default workspace: one per stream (calls on different
+    streams may overlap), shared by the calls of a stream whatever their
+    shape, grown in powers of two with outgrown buffers kept alive (a captured
+    graph may still point at them)."""
+    monkeypatch.setattr(amr, "_ws_cache", {})
+    a = amr._workspace("cpu", 0, 1000)
+    assert a.numel() == 1024 and int(a.sum()) == 0
+    assert amr._workspace("cpu", 0, 700).data_ptr() == a.data_ptr()  # a smaller shape reuses it
+    b = amr._workspace("cpu", 12345, 1000)  # another stream: a buffer of its own
+    assert b.data_ptr() != a.data_ptr()
+    c = amr._workspace("cpu", 0, 5000)  # outgrown: a larger buffer, the old one kept
+    assert c.numel() == 8192 and c.data_ptr() != a.data_ptr()
+    bufs = amr._ws_cache[("cpu", 0)]
+    assert [t.data_ptr() for t in bufs] == [a.data_ptr(), c.data_ptr()]
+    assert amr._workspace("cpu", 0, 1000).data_ptr() == c.data_ptr()
+    for n in range(1, 40000, 997):
+        amr._workspace("cpu", 7, n)
+    sizes = [t.numel() for t in amr._ws_cache[("cpu", 7)]]
+    assert sum(sizes) < 2 * sizes[-1] and all(s & (s - 1) == 0 for s in sizes)
