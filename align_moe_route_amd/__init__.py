@@ -158,6 +158,35 @@ def _workspace(device, stream_handle: int, nbytes: int):
     return bufs[-1]
 
 
+def _check_tensor(t, dev, dtype, n: int, name: str):
+    """t is a contiguous tensor of dtype (any dtype when None) with at least n
+    elements on dev; every pointer handed to the library comes through here or
+    through a check of the same kind, so no host address reaches a kernel."""
+    import torch
+    if not (isinstance(t, torch.Tensor) and t.device == dev and (dtype is None or t.dtype == dtype)
+            and t.is_contiguous() and t.numel() >= n):
+        what = "a" if dtype is None else f"a {dtype}"
+        raise ValueError(f"{name} must be {what} contiguous tensor of at least {n} elements on {dev}")
+
+
+def _check_metadata(sorted_ids, expert_of_block, num_post_pad, rows: int, blocks: int, dev):
+    import torch
+    for t, n, name in ((sorted_ids, rows, "sorted_ids"), (expert_of_block, blocks, "expert_of_block"),
+                       (num_post_pad, 1, "num_post_pad")):
+        _check_tensor(t, dev, torch.int32, n, name)
+
+
+def _check_route_output(out, M: int, k: int, rows: int, blocks: int, dev):
+    """A caller's RouteSortOutput: ids and weights exactly [M, k], the metadata
+    buffers at least their capacities, all contiguous on dev."""
+    import torch
+    for t, dtype, name in ((out.ids, torch.int32, "out.ids"), (out.weights, torch.float32, "out.weights")):
+        _check_tensor(t, dev, dtype, M * k, name)
+        if tuple(t.shape) != (M, k):
+            raise ValueError(f"{name} must have shape ({M}, {k})")
+    _check_metadata(out.sorted_ids, out.expert_of_block, out.num_post_pad, rows, blocks, dev)
+
+
 def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
                out: Optional[RouteSortOutput] = None, workspace=None, flags: int = 0,
                stats=None, stream=None, events=None, local=None) -> RouteSortOutput:
@@ -217,18 +246,16 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             torch.empty((1,), dtype=torch.int32, device=dev),
         )
     else:
-        for t, dtype, shape in ((out.ids, torch.int32, (M, k)), (out.weights, torch.float32, (M, k))):
-            if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
-                raise ValueError("out.ids / out.weights have the wrong dtype, shape or device")
-        if (out.sorted_ids.numel() < rows or out.expert_of_block.numel() < blocks or
-                out.sorted_ids.dtype != torch.int32 or out.expert_of_block.dtype != torch.int32 or
-                out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
-            raise ValueError("out metadata buffers too small or of the wrong dtype")
+        _check_route_output(out, M, k, rows, blocks, dev)
+    if stats is not None:
+        _check_tensor(stats, dev, torch.int32, 2, "stats")
     nbytes = workspace_bytes(M, E, k, block)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     if workspace is None:
         workspace = _workspace(dev, stream.cuda_stream, nbytes) if nbytes else None
+    else:
+        _check_tensor(workspace, dev, None, 0, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if local is not None:
@@ -264,6 +291,8 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
 def sigmoid_probe(x):
     """Both sigmoid forms of the kernels on a float32 GPU tensor (diagnostics)."""
     import torch
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.float32):
+        raise ValueError("x must be a float32 GPU tensor")
     x = x.contiguous()
     f = torch.empty_like(x)
     e = torch.empty_like(x)
@@ -278,6 +307,8 @@ def sigmoid_table_probe(bits):
     """Sigmoid of BF16 bit patterns (an int16/uint16-valued GPU tensor) through
     the kernels' LDS table: (single-value form, packed-pair form)."""
     import torch
+    if not (isinstance(bits, torch.Tensor) and bits.is_cuda):
+        raise ValueError("bits must be a GPU tensor")
     h = bits.contiguous().to(torch.int16)
     o1 = torch.empty(h.shape, dtype=torch.float32, device=h.device)
     o2 = torch.empty_like(o1)
@@ -312,15 +343,15 @@ def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, 
         out = SortOutput(torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
                          torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
                          torch.empty((1,), dtype=torch.int32, device=dev))
-    elif (out.sorted_ids.numel() < rows or out.expert_of_block.numel() < blocks or
-          out.sorted_ids.dtype != torch.int32 or out.expert_of_block.dtype != torch.int32 or
-          out.num_post_pad.dtype != torch.int32 or out.num_post_pad.numel() < 1):
-        raise ValueError("out buffers too small or of the wrong dtype")
+    else:
+        _check_metadata(out.sorted_ids, out.expert_of_block, out.num_post_pad, rows, blocks, dev)
     nbytes = workspace_bytes(M, E, k, block)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     if workspace is None:
         workspace = _workspace(dev, stream.cuda_stream, nbytes) if nbytes else None
+    else:
+        _check_tensor(workspace, dev, None, 0, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
@@ -356,11 +387,7 @@ def grouped_gemm1(x, w, sorted_ids, expert_of_block, num_post_pad, k: int, block
     blocks = max_blocks(M, E, k, block)
     if rows < 0:
         raise ValueError("invalid sizes or row capacity overflow")
-    for t, n, name in ((sorted_ids, rows, "sorted_ids"), (expert_of_block, blocks, "expert_of_block"),
-                       (num_post_pad, 1, "num_post_pad")):
-        if not (isinstance(t, torch.Tensor) and t.device == x.device and t.dtype == torch.int32
-                and t.is_contiguous() and t.numel() >= n):
-            raise ValueError(f"{name} must be a contiguous int32 tensor of at least {n} entries on x's device")
+    _check_metadata(sorted_ids, expert_of_block, num_post_pad, rows, blocks, x.device)
     if out is None:
         out = torch.empty((max(rows, 1), N), dtype=torch.bfloat16, device=x.device)
     elif not (out.device == x.device and out.dtype == torch.bfloat16 and out.is_contiguous()
@@ -418,6 +445,8 @@ def gate_route_sort(hidden, w_gate, bias, k: int, n_group: int, topk_group: int,
                               torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
                               torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
                               torch.empty((1,), dtype=torch.int32, device=dev))
+    else:
+        _check_route_output(out, M, k, rows, blocks, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     rc = int(lib().moe_gate_route_sort(hidden.data_ptr(), w_gate.data_ptr(), bias.data_ptr(), M, E, H, k, n_group,

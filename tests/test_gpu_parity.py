@@ -235,6 +235,31 @@ def test_zero_tokens():
     assert torch.all(out.sorted_ids == 7) and torch.all(out.expert_of_block == 7)
 
 
+def test_binding_refuses_host_buffers():
+    """Outputs, workspace or stats in host memory are refused before any
+    launch, by route_sort and by sort_from_ids."""
+    cfg = workloads.CONFIGS["tiny"]
+    x, b = to_gpu(workloads.make_inputs(cfg))
+    print(f"[gpu] host buffers refused, M={cfg.M} E={cfg.E}", flush=True)
+    good = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    torch.cuda.synchronize()
+    for field in good._fields:
+        out = good._replace(**{field: getattr(good, field).cpu()})
+        with pytest.raises(ValueError):
+            amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+    with pytest.raises(ValueError):
+        amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
+                       workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
+                       stats=torch.zeros(2, dtype=torch.int32))
+    srt = amr.sort_from_ids(good.ids, cfg.E, cfg.block)
+    torch.cuda.synchronize()
+    for field in srt._fields:
+        with pytest.raises(ValueError):
+            amr.sort_from_ids(good.ids, cfg.E, cfg.block, out=srt._replace(**{field: getattr(srt, field).cpu()}))
+
+
 def test_determinism_across_runs_and_paths():
     cfg = workloads.custom(700, 896, 16, 8, 4, 128, "bf16", "log_zipf", seed=21)
     inp = workloads.make_inputs(cfg)

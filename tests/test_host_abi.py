@@ -263,3 +263,33 @@ def test_default_workspace_per_stream(monkeypatch):
         amr._workspace("cpu", 7, n)
     sizes = [t.numel() for t in amr._ws_cache[("cpu", 7)]]
     assert sum(sizes) < 2 * sizes[-1] and all(s & (s - 1) == 0 for s in sizes)
+
+
+def test_binding_rejects_buffers_before_any_call():
+    """The binding's tensor checks (run before any library call): a buffer on
+    another device, of another dtype, too small or not contiguous is refused,
+    so no host address or short buffer reaches a kernel."""
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cpu")
+    M, k, rows, blocks = 3, 2, 40, 5
+    good = amr.RouteSortOutput(torch.zeros((M, k), dtype=torch.int32), torch.zeros((M, k)),
+                               torch.zeros(rows, dtype=torch.int32), torch.zeros(blocks, dtype=torch.int32),
+                               torch.zeros(1, dtype=torch.int32))
+    amr._check_route_output(good, M, k, rows, blocks, dev)
+    bad = [
+        good._replace(sorted_ids=torch.zeros(rows, dtype=torch.int32, device="meta")),  # another device
+        good._replace(expert_of_block=torch.zeros(blocks - 1, dtype=torch.int32)),     # too small
+        good._replace(num_post_pad=torch.zeros(1, dtype=torch.int64)),                 # wrong dtype
+        good._replace(sorted_ids=torch.zeros(2 * rows, dtype=torch.int32)[::2]),       # strided view
+        good._replace(ids=torch.zeros((k, M), dtype=torch.int32)),                     # wrong shape
+        good._replace(weights=torch.zeros((M, k), dtype=torch.float64)),              # wrong dtype
+        good._replace(ids=torch.zeros((M, k), dtype=torch.int32, device="meta")),      # another device
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            amr._check_route_output(out, M, k, rows, blocks, dev)
+    with pytest.raises(ValueError):
+        amr._check_tensor(torch.zeros(4, device="meta"), dev, None, 0, "workspace")
+    with pytest.raises(ValueError):
+        amr._check_tensor(torch.zeros(1, dtype=torch.int32), dev, torch.int32, 2, "stats")
+    amr._check_tensor(torch.zeros(2, dtype=torch.int32), dev, torch.int32, 2, "stats")
