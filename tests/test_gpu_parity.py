@@ -186,6 +186,122 @@ def test_sweep_parity_single_workgroup(case):
     assert_parity(inp, run(inp, flags=amr.FLAG_FORCE_SINGLE_WG))
 
 
+# Drawn once by seeded generators and kept as a fixed list.  The first 32 range
+# over the whole contract (E from 64 to 4096 with odd sizes, n_group any
+# divisor, topk_group and k anywhere in range, block 1 to 256, M log-uniform up
+# to 6000); the other 64 over the wave layouts (E = 32 or 64 lanes times 1 to
+# 64 experts per lane, n_group dividing the lanes, M up to 20000); both dtypes
+# and every distribution.
+RANDOM_SWEEP = [
+    (14, 192, 4, 32, 3, 128, "bf16", "coarse"),
+    (4, 4096, 56, 2, 1, 1, "bf16", "shared"),
+    (213, 192, 38, 3, 2, 256, "f32", "dominant_group"),
+    (4853, 640, 2, 80, 1, 24, "bf16", "duplicated"),
+    (6, 512, 21, 32, 12, 100, "f32", "duplicated"),
+    (10, 192, 54, 48, 42, 3, "bf16", "duplicated"),
+    (1, 448, 18, 7, 1, 100, "f32", "coarse"),
+    (838, 192, 40, 8, 8, 8, "f32", "dominant_group"),
+    (2475, 512, 62, 16, 8, 3, "f32", "hot"),
+    (123, 192, 9, 24, 5, 128, "bf16", "shared"),
+    (376, 96, 4, 48, 5, 2, "f32", "normal"),
+    (19, 64, 35, 2, 2, 8, "bf16", "hot"),
+    (18, 999, 37, 9, 6, 2, "f32", "log_zipf"),
+    (38, 160, 32, 160, 81, 32, "bf16", "shared"),
+    (17, 4096, 4, 4096, 2239, 64, "bf16", "offset_normal"),
+    (8, 768, 3, 1, 1, 256, "f32", "log_zipf"),
+    (34, 64, 21, 1, 1, 1, "bf16", "dominant_group"),
+    (53, 64, 46, 1, 1, 64, "bf16", "equal"),
+    (35, 128, 36, 64, 52, 16, "bf16", "log_zipf"),
+    (3, 128, 14, 4, 1, 64, "bf16", "shared"),
+    (3, 100, 16, 5, 2, 3, "bf16", "dominant_group"),
+    (11, 640, 49, 5, 4, 1, "bf16", "coarse"),
+    (6, 640, 32, 640, 57, 32, "bf16", "shared"),
+    (207, 512, 19, 4, 2, 24, "bf16", "hot"),
+    (68, 64, 37, 16, 15, 3, "f32", "offset_normal"),
+    (8, 2048, 51, 16, 1, 16, "bf16", "equal"),
+    (84, 768, 57, 24, 16, 128, "f32", "offset_normal"),
+    (1053, 257, 32, 257, 49, 8, "f32", "coarse"),
+    (5, 160, 61, 20, 19, 32, "bf16", "shared"),
+    (172, 256, 9, 8, 2, 8, "f32", "hot"),
+    (134, 96, 29, 2, 1, 16, "bf16", "coarse"),
+    (3, 2560, 10, 8, 7, 100, "f32", "dominant_group"),
+    (3990, 1024, 62, 32, 13, 128, "bf16", "coarse"),
+    (807, 64, 16, 4, 2, 200, "bf16", "hot"),
+    (4, 256, 51, 4, 1, 4, "f32", "coarse"),
+    (17, 768, 57, 2, 1, 16, "f32", "offset_normal"),
+    (347, 128, 38, 1, 1, 32, "bf16", "dominant_group"),
+    (122, 128, 19, 4, 2, 200, "bf16", "equal"),
+    (15, 4096, 51, 32, 28, 200, "bf16", "offset_normal"),
+    (4591, 64, 12, 32, 10, 200, "bf16", "dominant_group"),
+    (3062, 256, 20, 4, 2, 7, "f32", "offset_normal"),
+    (2929, 4096, 17, 8, 4, 4, "bf16", "dominant_group"),
+    (24, 768, 58, 2, 1, 64, "f32", "normal"),
+    (9375, 1280, 63, 32, 28, 128, "bf16", "shared"),
+    (46, 4096, 9, 4, 4, 200, "f32", "log_zipf"),
+    (116, 256, 8, 8, 5, 64, "bf16", "log_zipf"),
+    (5, 192, 59, 1, 1, 1, "f32", "duplicated"),
+    (11718, 1024, 27, 1, 1, 32, "bf16", "offset_normal"),
+    (239, 128, 20, 16, 4, 200, "bf16", "normal"),
+    (28, 1792, 61, 2, 2, 200, "bf16", "log_zipf"),
+    (821, 128, 4, 2, 1, 16, "f32", "normal"),
+    (3489, 256, 3, 32, 1, 32, "bf16", "dominant_group"),
+    (10, 256, 7, 2, 1, 200, "bf16", "log_zipf"),
+    (654, 896, 18, 16, 2, 7, "bf16", "duplicated"),
+    (86, 1280, 15, 1, 1, 7, "bf16", "equal"),
+    (95, 512, 41, 8, 3, 128, "bf16", "dominant_group"),
+    (1, 896, 47, 2, 1, 32, "bf16", "hot"),
+    (229, 1792, 36, 16, 16, 7, "bf16", "dominant_group"),
+    (6, 512, 5, 64, 40, 32, "bf16", "normal"),
+    (150, 512, 21, 1, 1, 128, "f32", "offset_normal"),
+    (56, 512, 40, 4, 1, 16, "f32", "coarse"),
+    (1, 192, 23, 4, 2, 64, "bf16", "normal"),
+    (793, 64, 1, 64, 1, 4, "f32", "duplicated"),
+    (20, 512, 44, 4, 3, 1, "bf16", "equal"),
+    (22, 256, 61, 8, 6, 16, "f32", "log_zipf"),
+    (14499, 128, 7, 4, 1, 7, "f32", "log_zipf"),
+    (8, 3072, 19, 64, 18, 16, "bf16", "equal"),
+    (44, 128, 24, 2, 1, 64, "bf16", "offset_normal"),
+    (2491, 768, 41, 4, 2, 4, "f32", "log_zipf"),
+    (3, 512, 30, 2, 2, 128, "f32", "equal"),
+    (14, 1024, 47, 8, 5, 200, "f32", "offset_normal"),
+    (13, 128, 26, 2, 2, 7, "f32", "duplicated"),
+    (1, 64, 9, 1, 1, 200, "f32", "normal"),
+    (3459, 1024, 3, 16, 12, 32, "bf16", "offset_normal"),
+    (1, 4096, 58, 16, 5, 200, "bf16", "equal"),
+    (31, 1792, 20, 1, 1, 128, "bf16", "offset_normal"),
+    (1547, 64, 49, 32, 32, 128, "f32", "log_zipf"),
+    (4, 128, 31, 1, 1, 128, "f32", "hot"),
+    (6, 192, 23, 8, 1, 64, "bf16", "duplicated"),
+    (2929, 4096, 27, 4, 3, 1, "f32", "duplicated"),
+    (704, 896, 49, 8, 7, 200, "f32", "shared"),
+    (13217, 896, 9, 1, 1, 1, "f32", "normal"),
+    (18, 128, 24, 1, 1, 200, "f32", "shared"),
+    (97, 896, 61, 8, 4, 128, "f32", "duplicated"),
+    (72, 256, 24, 1, 1, 64, "f32", "offset_normal"),
+    (7451, 512, 13, 8, 4, 7, "bf16", "log_zipf"),
+    (1, 896, 4, 2, 2, 64, "bf16", "duplicated"),
+    (228, 2048, 41, 1, 1, 1, "f32", "normal"),
+    (307, 896, 20, 64, 12, 32, "f32", "log_zipf"),
+    (7, 64, 19, 1, 1, 1, "f32", "dominant_group"),
+    (1, 2240, 6, 1, 1, 32, "f32", "coarse"),
+    (18502, 256, 52, 4, 3, 4, "bf16", "hot"),
+    (12, 1280, 26, 2, 1, 16, "bf16", "log_zipf"),
+    (6, 1024, 37, 1, 1, 32, "bf16", "equal"),
+    (63, 256, 11, 32, 12, 16, "bf16", "shared"),
+    (5, 896, 33, 4, 2, 64, "f32", "duplicated"),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_SWEEP, ids=lambda c: "M{}_E{}_k{}_g{}-{}_b{}_{}_{}".format(*c))
+def test_random_sweep_parity(case):
+    M, E, k, ng, tg, block, dtype, dist = case
+    cfg = workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=M * 7 + E)
+    inp = workloads.make_inputs(cfg)
+    assert_parity(inp, run(inp))
+    if M <= 64:
+        assert_parity(inp, run(inp, flags=amr.FLAG_FORCE_SINGLE_WG))
+
+
 @pytest.mark.parametrize("dist", ["normal", "hot", "shared", "dominant_group", "log_zipf", "equal",
                                   "duplicated", "coarse"])
 def test_distributions_prefill_shape(dist):
