@@ -75,6 +75,54 @@ def test_rows_repeating_an_expert(M, E, k, block):
     run_and_check(ids, E, block)
 
 
+# Drawn once by a seeded generator and kept as a fixed list:
+# M, E, k, block, share of dropped ids, rows may repeat an expert, Zipf skew.
+RANDOM_IDS = [
+    (11, 1, 1, 128, 0.5, False, 0.8),
+    (2795, 4096, 21, 2, 0.0, False, 1.3),
+    (396, 100, 47, 128, 0.5, False, 0.0),
+    (16105, 1000, 24, 2, 0.05, False, 0.0),
+    (28, 3, 1, 2, 0.0, False, 0.8),
+    (6, 64, 25, 32, 0.5, True, 0.0),
+    (1, 100, 5, 300, 0.0, False, 1.3),
+    (7, 3, 45, 128, 0.0, True, 0.0),
+    (79, 1000, 28, 128, 0.5, True, 0.0),
+    (518, 896, 52, 2, 0.0, False, 0.0),
+    (1980, 896, 30, 1, 0.0, True, 0.0),
+    (107, 64, 29, 2, 0.5, True, 0.0),
+    (9156, 4096, 50, 2, 0.0, False, 0.0),
+    (4, 64, 33, 128, 0.5, True, 0.0),
+    (1714, 512, 63, 5, 0.05, False, 0.0),
+    (71, 896, 3, 300, 0.5, False, 0.8),
+    (874, 4096, 53, 128, 0.0, False, 1.3),
+    (2388, 1000, 20, 128, 0.5, False, 1.3),
+    (6141, 1, 50, 5, 0.05, True, 0.0),
+    (101, 257, 4, 32, 0.5, False, 0.8),
+    (4178, 64, 35, 2, 0.5, False, 1.3),
+    (19, 1000, 42, 5, 0.5, True, 0.0),
+    (72, 3, 3, 128, 0.0, False, 0.0),
+    (43, 1000, 25, 128, 0.0, True, 0.0),
+    (1, 2048, 64, 5, 0.0, False, 0.8),
+    (17752, 128, 2, 1, 0.05, True, 0.0),
+    (221, 1, 1, 16, 0.5, False, 0.8),
+    (2, 896, 12, 1, 0.05, True, 0.0),
+    (41, 896, 50, 2, 0.0, True, 0.0),
+    (1097, 1, 1, 5, 0.05, False, 0.8),
+    (2730, 1000, 8, 2, 0.0, False, 1.3),
+    (2434, 896, 34, 300, 0.0, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_IDS, ids=lambda c: "M{}_E{}_k{}_b{}_drop{}_rep{}_skew{}".format(*c))
+def test_random_ids(case):
+    M, E, k, block, drop, repeat, skew = case
+    rng = np.random.default_rng(M * 31 + E * 7 + k)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32) if repeat else distinct_rows(rng, M, E, k, skew)
+    if drop > 0:
+        mask = rng.random(ids.shape) < drop
+        ids[mask] = rng.choice(np.array([-1, E, -2 ** 31, 2 ** 31 - 1]), size=int(mask.sum()))
+    run_and_check(ids, E, block)
+
 def test_matches_full_route_sort():
     cfg = workloads.custom(3000, 896, 16, 8, 4, 128, "bf16", "log_zipf", seed=12)
     inp = workloads.make_inputs(cfg)
