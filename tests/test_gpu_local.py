@@ -94,3 +94,40 @@ def test_rank_with_no_routes_and_untouched_tails():
     torch.cuda.synchronize()
     assert int(out.num_post_pad.item()) == 0
     assert bool((out.sorted_ids == -77).all()) and bool((out.expert_of_block == -77).all())
+
+
+# Drawn once by a seeded generator over the wave layouts and kept as a fixed
+# list: M, E, k, n_group, topk_group, block, dtype, distribution, then two
+# expert ranges (begin, count), the second one ending at E.
+RANDOM_LOCAL = [
+    (5, 896, 7, 32, 22, 4, "bf16", "shared", 19, 859, 217, 679),
+    (10, 64, 20, 1, 1, 200, "bf16", "coarse", 4, 37, 31, 33),
+    (298, 64, 31, 8, 5, 64, "bf16", "normal", 3, 61, 2, 62),
+    (1252, 2240, 59, 64, 29, 128, "f32", "hot", 270, 1378, 967, 1273),
+    (8, 1280, 23, 16, 6, 200, "bf16", "equal", 128, 832, 49, 1231),
+    (872, 128, 62, 4, 3, 16, "f32", "dominant_group", 20, 71, 68, 60),
+    (14527, 64, 19, 1, 1, 7, "bf16", "log_zipf", 35, 7, 42, 22),
+    (1227, 512, 39, 16, 3, 7, "f32", "coarse", 10, 477, 386, 126),
+    (142, 768, 12, 1, 1, 4, "bf16", "hot", 94, 463, 504, 264),
+    (5700, 896, 37, 4, 4, 16, "bf16", "coarse", 375, 351, 653, 243),
+    (1, 3072, 24, 2, 2, 1, "bf16", "normal", 100, 2787, 693, 2379),
+    (3267, 896, 44, 16, 1, 1, "f32", "offset_normal", 40, 839, 557, 339),
+    (1163, 64, 4, 8, 2, 7, "f32", "dominant_group", 17, 43, 15, 49),
+    (244, 64, 28, 8, 4, 64, "bf16", "normal", 5, 3, 44, 20),
+    (9, 4096, 42, 64, 20, 4, "bf16", "equal", 1856, 1455, 3724, 372),
+    (122, 1792, 48, 8, 2, 7, "f32", "duplicated", 781, 811, 197, 1595),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_LOCAL, ids=lambda c: "M{}_E{}_k{}_g{}-{}_b{}_{}_{}_r{}+{}_r{}+{}".format(*c))
+def test_random_shapes_and_ranges(case):
+    M, E, k, ng, tg, block, dtype, dist, lb1, lc1, lb2, lc2 = case
+    cfg = workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=M * 5 + E, name="random")
+    inp = workloads.make_inputs(cfg)
+    ref = orc.route_sort(inp.logits_storage, cfg.dtype, inp.bias, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    x, b = to_gpu(inp)
+    full = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
+    torch.cuda.synchronize()
+    assert np.array_equal(full.ids.cpu().numpy(), ref.ids)
+    for lb, lc in ((lb1, lc1), (lb2, lc2)):
+        check_rank(cfg, x, b, ref.ids, full.ids, full.weights, lb, lc)
