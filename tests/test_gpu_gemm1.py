@@ -63,6 +63,22 @@ SHAPES = [  # M, E, k, K, N, block
     (97, 40, 5, 64, 128, 96),
     (150, 12, 4, 64, 512, 64),     # one K step; 64 x 256 tiles
     (90, 20, 3, 128, 256, 256),    # two 128-row tiles per padding block
+    # drawn once by a seeded generator (K a multiple of 64 up to 1024, N a
+    # multiple of 128 up to 768, block a multiple of 32 up to 256) and kept
+    (675, 13, 11, 832, 256, 96),
+    (493, 51, 4, 128, 128, 64),
+    (308, 56, 11, 704, 128, 32),
+    (162, 47, 10, 576, 768, 32),
+    (375, 34, 2, 448, 384, 160),
+    (610, 35, 9, 64, 512, 96),
+    (462, 54, 15, 128, 768, 256),
+    (544, 18, 2, 256, 384, 160),
+    (601, 34, 16, 128, 384, 32),
+    (13, 27, 7, 960, 384, 128),
+    (3, 14, 10, 128, 768, 128),    # a few tokens: nearly every tile is padding
+    (1, 29, 11, 768, 512, 64),
+    (2, 36, 14, 64, 512, 96),
+    (10, 61, 13, 704, 512, 256),
 ]
 
 
