@@ -26,6 +26,18 @@ CASES = [  # M, E, H, k, n_group, topk_group, block
     (64, 64, 256, 8, 1, 1, 8),
     (3, 4096, 1024, 16, 16, 8, 128),
     (2, 160, 8, 6, 4, 2, 5),
+    # drawn once by a seeded generator (M up to 64, H any multiple of 8,
+    # groups, k and block anywhere in range) and kept
+    (39, 896, 528, 55, 7, 1, 16),
+    (33, 64, 7920, 17, 2, 1, 1),
+    (25, 1024, 2328, 51, 16, 9, 32),
+    (61, 4096, 16, 58, 32, 10, 64),
+    (38, 128, 3616, 16, 32, 10, 64),
+    (50, 1024, 240, 64, 16, 15, 64),
+    (5, 128, 3400, 15, 8, 4, 128),
+    (39, 64, 3336, 25, 8, 5, 128),
+    (52, 96, 5768, 35, 48, 44, 16),
+    (19, 384, 1816, 31, 1, 1, 16),
 ]
 
 
