@@ -409,6 +409,30 @@ def test_graph_replay_with_changed_inputs():
         assert_parity(inp, g)
 
 
+def test_one_workspace_across_shapes():
+    """One workspace serves calls of different shapes in turn (three launches,
+    two launches with the folded scan, the sort-only entry, a smaller call after
+    a larger one): no call reads workspace words that an earlier call left."""
+    cfgs = [workloads.custom(6000, 896, 16, 8, 4, 128, "bf16", "log_zipf", seed=50),
+            workloads.custom(100, 512, 8, 4, 2, 32, "f32", "hot", seed=51),
+            workloads.custom(3000, 2048, 32, 16, 8, 64, "f32", "normal", seed=52),
+            workloads.custom(180, 896, 16, 8, 4, 16, "bf16", "shared", seed=53)]
+    need = max(amr.workspace_bytes(c.M, c.E, c.k, c.block) for c in cfgs)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for cfg in cfgs:
+            inp = workloads.make_inputs(cfg)
+            x, b = to_gpu(inp)
+            print(f"[gpu] shared workspace, pass {rep}, M={cfg.M} E={cfg.E} k={cfg.k}", flush=True)
+            out = amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, workspace=ws)
+            ref = assert_parity(inp, fetch(out, cfg.block))
+            srt = amr.sort_from_ids(out.ids, cfg.E, cfg.block, workspace=ws)
+            torch.cuda.synchronize()
+            npp = int(srt.num_post_pad.item())
+            assert npp == ref.meta.num_post_pad
+            assert np.array_equal(srt.sorted_ids[:npp].cpu().numpy(), ref.meta.sorted_ids)
+
+
 def test_concurrent_streams_default_workspace():
     """Calls queued on two streams, free to overlap in time, each with the
     binding's default workspace (one per stream): both match the oracle."""
