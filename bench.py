@@ -440,8 +440,9 @@ def main():
     if args.write_traffic:
         base = (f"python3 bench.py --workload {args.workload} --no-extra --no-cpu-baseline --steps 5 "
                 f"--warmup 1 --calib-copy-mb {args.calib_copy_mb:g}")
-        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- {base}"
-                for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+        # the commands as they made the two files: output folder = each file's folder
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(f) or '.'} -o run -- {base}"
+                for c, f in (("FETCH_SIZE", args.write_traffic[0]), ("WRITE_SIZE", args.write_traffic[1]))]
         for path in write_traffic_record(args.write_traffic[0], args.write_traffic[1], args.workload,
                                          args.calib_copy_mb, cmds):
             print(path)
