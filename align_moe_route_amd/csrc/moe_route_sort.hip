@@ -57,6 +57,7 @@
 
 #include "moe_route_sort.h"
 #include "route_internal.h"
+#include "sigmoid_rn.h"
 
 namespace {
 
@@ -98,6 +99,7 @@ struct Args {
   int nwg;     // workgroups of the multi-workgroup path
   int fast;    // the wave layout covers this shape
   int tbl;     // BF16 logits: keys from the sigmoid table in LDS (exact)
+  const float* sigtab;  // the table in device memory (copied into LDS by every workgroup)
   int bias_dma;  // bias is copied into LDS by DMA (16-byte aligned, E % 4 == 0)
   int rows_first;  // issue the row copies before the shared data (latency-bound calls)
   int gstage;  // the group stage changes the result (1 < topk_group < n_group, G > 1)
@@ -115,6 +117,12 @@ struct Args {
   int32_t* stats;
   const int32_t* in_ids;  // sort-only entry: caller's expert ids [M, k]
   int e_lo, EL;  // experts [e_lo, e_lo + EL) get metadata (all E unless a local range is asked for)
+  // sort-only entry with caller counters: counters[e] rows already head expert
+  // e's segment; ws_c0 is the workspace copy the kernels read; cap is the
+  // caller's row capacity.  counters == nullptr: no counters.
+  int32_t* counters;
+  int32_t* ws_c0;
+  int cap;
 };
 
 // ----------------------------------------------------------------------------
@@ -137,7 +145,7 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
   if (kind != KIND_SCATTER) p.bits = take((size_t)E * 8);
   p.redd = take((size_t)kNW * 8);
   if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
-  if (kind == KIND_SCATTER) p.cpre = take((size_t)E * 8);  // column prefixes, then counts
+  if (kind == KIND_SCATTER) p.cpre = take((size_t)E * 12);  // column prefixes, counts, initial counters
   if (kind != KIND_SCATTER) {
     p.ids = take((size_t)tw * k * 4);
     p.bias = take((size_t)E * 4);
@@ -256,35 +264,9 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Correctly rounded FP32 sigmoid.  For |x| < 2^-10 the float64 quotient can
-// land exactly on an FP32 rounding midpoint (0.5 + x/4 is one for many BF16
-// x) while the cubic term, below float64 resolution at 0.5, decides the side;
-// there the series 1/2 + x/4 - x^3/48 + x^5/480 is split into an exact head
-// and a small tail and the rounding side is read off their sum.  Elsewhere
-// RN32 of the float64 value 1 / (1 + exp(-x)).
-__device__ __forceinline__ float sigmoid_exact(float x) {
-  const double xd = (double)x;
-  if (fabs(xd) < 0x1p-10) {
-    const double hi = 0.5 + 0.25 * xd;  // exact for |x| >= 2^-29; else far from a midpoint
-    const double x2 = xd * xd;
-    const double lo = xd * x2 * (-1.0 / 48.0 + x2 * (1.0 / 480.0));
-    const float f = (float)hi;
-    const double fb = (double)f;
-    if (fb == hi) return f;
-    const uint32_t fu = __float_as_uint(f);
-    const float g = __uint_as_float(fb > hi ? fu - 1u : fu + 1u);  // other neighbour of hi
-    const double gb = (double)g;
-    const double mid = 0.5 * (fb + gb);
-    const double d = (hi - mid) + lo;  // side of the midpoint the exact value lies on
-    const float up = fb > gb ? f : g;
-    const float dn = fb > gb ? g : f;
-    if (d > 0.0) return up;
-    if (d < 0.0) return dn;
-    return (__float_as_uint(up) & 1u) ? dn : up;
-  }
-  const double e = exp(-xd);
-  return (float)(1.0 / (1.0 + e));
-}
+// Correctly rounded FP32 sigmoid (sigmoid_rn.h: float64 quotient, with the
+// rare inputs near an FP32 rounding midpoint settled in double-double).
+__device__ __forceinline__ float sigmoid_exact(float x) { return sigrn::sigmoid_rn32(x); }
 
 // The sigmoid table (built once per device by k_build_sig_table from
 // sigmoid_exact, copied into LDS offset 0 by every workgroup that uses it).
@@ -747,8 +729,21 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     put_key(i, sig_lds(o0) + bias_of(i));
     put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
   };
+  // exact keys: RN32 of the float64 sigmoid.  A quotient that lies near an
+  // FP32 rounding midpoint makes the key +inf (no real key is infinite); the
+  // token is then sent to the workgroup path, which settles it exactly, and
+  // the double-double settlement stays out of this unrolled loop
   auto put = [&](int i, float x) {  // FP32 logit of expert i
-    put_key(i, (exact ? sigmoid_exact(x) : sigmoid_fast(x)) + bias_of(i));
+    float s;
+    if (exact) {
+      bool amb;
+      float up;
+      s = sigrn::sigmoid_rn32_try(x, amb, up);
+      s = amb ? INFINITY : s;
+    } else {
+      s = sigmoid_fast(x);
+    }
+    put_key(i, s + bias_of(i));
     if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
   };
   if (EPL == 0) {  // slots past epl stay defined (their candidate bits are masked off)
@@ -912,7 +907,8 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   float thr = s2f(T);
   if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
   const bool ok = (NSEG == 1 || seg == 0) ? okseg[0] : okseg[NSEG - 1];
-  int status = !act ? TOK_ESCALATE : (!ok ? TOK_ESCALATE : (redo ? TOK_REDO_EXACT : TOK_DONE));
+  const bool amb_seg = exact && !BF16 && seg_max_u32<SEG>(f2s(lm)) == f2s(INFINITY);
+  int status = !act ? TOK_ESCALATE : ((!ok || amb_seg) ? TOK_ESCALATE : (redo ? TOK_REDO_EXACT : TOK_DONE));
 
   // ---- 4. candidates (keys >= thr), compacted in expert order ----
   // The sign of key - thr is 1 exactly when key < thr (keys are never -0 and a
@@ -1026,7 +1022,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
   }
   if (a.tbl) {
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(g_sig_table);
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.sigtab);
 #pragma unroll
     for (int j = 0; j * kWG * 16 < kSigBytes; ++j)
       __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
@@ -1331,7 +1327,13 @@ __global__ __launch_bounds__(kWG) void k_colscan(Args a) {
   }
   if (w == 0) {
     a.ws_tot[e] = total;
-    a.ws_pad[e] = pad_block(total, a);
+    if (a.counters) {  // -1 marks a negative counter or a segment past the capacity
+      const int c0 = a.ws_c0[e];
+      const long long t = (long long)total + c0;
+      a.ws_pad[e] = (c0 < 0 || t > a.cap) ? -1 : pad_block((int)t, a);
+    } else {
+      a.ws_pad[e] = pad_block(total, a);
+    }
   }
 }
 
@@ -1366,8 +1368,17 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
     rv[j] = q < ns ? rec[q] : 0;
   }
   // cnt: counts of the experts this block pads (at e - es0), or, folded, of
-  // every expert (at e)
+  // every expert (at e); c0s: the caller's initial counters (sort-only entry)
   int* cnt = L.cpre + a.E;
+  int* c0s = L.cpre + 2 * a.E;
+  if (a.counters)
+    for (int e = tid; e < a.E; e += kWG) c0s[e] = a.ws_c0[e];
+  // padded size of a segment holding t routes after c0 caller rows; -1 when c0
+  // is negative or the segment alone passes the caller's capacity
+  auto padc = [&](int t, int c0) {
+    const long long n = (long long)t + c0;
+    return (c0 < 0 || n > a.cap) ? -1 : pad_block((int)n, a);
+  };
   if (a.fold) {
     // the column prefix of this block (rows before it) and every expert's
     // total, from the raw histogram rows
@@ -1391,7 +1402,7 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
 #pragma unroll
     for (int i = 0; i < kEPerThread; ++i) {
       const int e = tid * ept + i;
-      pv[i] = (i < ept && e < a.E) ? pad_block(cnt[e], a) : 0;
+      pv[i] = (i < ept && e < a.E) ? (a.counters ? padc(cnt[e], c0s[e]) : pad_block(cnt[e], a)) : 0;
     }
   } else {
     int cv[kEPerThread], tv[kEPerThread];
@@ -1408,6 +1419,17 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
       const int e2 = tid + i * kWG;
       if (e2 < a.E) L.cpre[e2] = cv[i];
       if (es0 + e2 < es1) cnt[e2] = tv[i];
+    }
+  }
+  if (a.counters) {
+    // every block reaches the same verdict; on a negative counter or a total
+    // past the capacity nothing is written but num_post_pad = -1
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < kEPerThread; ++i) part += pv[i] < 0 ? 1e18 : (double)pv[i];
+    if (wg_sum_d(L, part) > (double)a.cap) {
+      if (w == 0 && tid == 0) *a.npp = -1;
+      return;
     }
   }
   // exclusive scan of the padded totals over all experts
@@ -1431,7 +1453,7 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   // one wave per expert of this block's share: padding rows, expert_of_block
   const int lane = lane_id();
   for (int e = es0 + (tid >> 6); e < es1; e += kNW) {
-    const int c = cnt[a.fold ? e : e - es0];
+    const int c = cnt[a.fold ? e : e - es0] + (a.counters ? c0s[e] : 0);
     const int o = L.off[e];
     const int p = (e + 1 < a.E ? L.off[e + 1] : total) - o;
     for (int r = c + lane; r < p; r += kWave) a.sorted_ids[o + r] = sentinel;
@@ -1443,9 +1465,11 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
     const int q = tid + j * kWG;
     if (q < ns && rv[j] >= 0) {  // a negative record is a dropped route (sort-only entry)
       const int e = rv[j] & 0xFFFF;
-      a.sorted_ids[L.off[e] + L.cpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
+      a.sorted_ids[L.off[e] + (a.counters ? c0s[e] : 0) + L.cpre[e] + (rv[j] >> 16)] = t0 * a.k + q;
     }
   }
+  if (a.counters && w == 0)  // every block read the initial values from the workspace copy
+    for (int e = tid; e < a.E; e += kWG) a.counters[e] = c0s[e] + (a.fold ? cnt[e] : a.ws_tot[e]);
 }
 
 // ----------------------------------------------------------------------------
@@ -1458,31 +1482,40 @@ struct IdsLds {
   int* cnt;                  // [E] routes of the workgroup per expert
   int* rec;                  // [tw*k] expert | rank << 16, or -1 for a dropped route
   int* off;                  // [E] expert offsets (single-workgroup kernel)
+  int* c0;                   // [E] the caller's initial counters (single-workgroup kernel)
+  double* redd;              // [kNW] partial sums
   int* misc;
   int* scan;
 };
-__host__ __device__ inline size_t ids_lds_bytes(int E, int tw, int k, size_t* o_cnt, size_t* o_rec, size_t* o_off,
-                                                size_t* o_misc, size_t* o_scan) {
+struct IdsPlan {
+  size_t cnt, rec, off, c0, redd, misc, scan, total;
+};
+__host__ __device__ inline IdsPlan ids_lds_plan(int E, int tw, int k) {
+  IdsPlan p{};
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
   take((size_t)E * 8);
-  *o_cnt = take((size_t)E * 4);
-  *o_rec = take((size_t)tw * k * 4);
-  *o_off = take((size_t)E * 4);
-  *o_misc = take(16 * 4);
-  *o_scan = take((size_t)kNW * 4);
-  return o;
+  p.cnt = take((size_t)E * 4);
+  p.rec = take((size_t)tw * k * 4);
+  p.off = take((size_t)E * 4);
+  p.c0 = take((size_t)E * 4);
+  p.redd = take((size_t)kNW * 8);
+  p.misc = take(16 * 4);
+  p.scan = take((size_t)kNW * 4);
+  p.total = o;
+  return p;
 }
 __device__ inline IdsLds ids_carve(const Args& a) {
-  size_t oc, orc, oo, om, osc;
-  ids_lds_bytes(a.E, a.tw, a.k, &oc, &orc, &oo, &om, &osc);
+  const IdsPlan p = ids_lds_plan(a.E, a.tw, a.k);
   IdsLds L;
   L.bits = reinterpret_cast<unsigned long long*>(g_lds);
-  L.cnt = reinterpret_cast<int*>(g_lds + oc);
-  L.rec = reinterpret_cast<int*>(g_lds + orc);
-  L.off = reinterpret_cast<int*>(g_lds + oo);
-  L.misc = reinterpret_cast<int*>(g_lds + om);
-  L.scan = reinterpret_cast<int*>(g_lds + osc);
+  L.cnt = reinterpret_cast<int*>(g_lds + p.cnt);
+  L.rec = reinterpret_cast<int*>(g_lds + p.rec);
+  L.off = reinterpret_cast<int*>(g_lds + p.off);
+  L.c0 = reinterpret_cast<int*>(g_lds + p.c0);
+  L.redd = reinterpret_cast<double*>(g_lds + p.redd);
+  L.misc = reinterpret_cast<int*>(g_lds + p.misc);
+  L.scan = reinterpret_cast<int*>(g_lds + p.scan);
   return L;
 }
 
@@ -1541,6 +1574,8 @@ __device__ void ids_local(const Args& a, const IdsLds& L, int t0, int nt) {
 __global__ __launch_bounds__(kWG) void k_ids_hist(Args a) {
   const IdsLds L = ids_carve(a);
   const int w = blockIdx.x;
+  if (a.counters && w == 0)  // the later launches read this copy; the last one advances the counters
+    for (int e = threadIdx.x; e < a.E; e += kWG) a.ws_c0[e] = a.counters[e];
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
   ids_local(a, L, t0, nt);
@@ -1550,16 +1585,48 @@ __global__ __launch_bounds__(kWG) void k_ids_hist(Args a) {
   for (int q = threadIdx.x; q < ns; q += kWG) rec[q] = L.rec[q];
 }
 
-// M <= 64: the whole sort in one workgroup.
+// M <= 64: the whole sort in one workgroup.  With caller counters, expert e's
+// segment holds counters[e] caller rows first (not written), the counters are
+// read before anything is written and advanced at the end; a negative counter
+// or a total past the capacity writes num_post_pad = -1 and nothing else.
 __global__ __launch_bounds__(kWG) void k_ids_small(Args a) {
   const IdsLds L = ids_carve(a);
   const int tid = threadIdx.x;
-  ids_local(a, L, 0, a.M);
+  if (a.counters)
+    for (int e = tid; e < a.E; e += kWG) L.c0[e] = a.counters[e];
+  ids_local(a, L, 0, a.M);  // ends with a barrier
+  auto c0_of = [&](int e) { return a.counters ? L.c0[e] : 0; };
+  // padded size of expert e's segment; -1 for a negative counter or a
+  // segment past the capacity
+  auto padded = [&](int e) {
+    if (!a.counters) return pad_block(L.cnt[e], a);
+    const int c0 = L.c0[e];
+    const long long n = (long long)L.cnt[e] + c0;
+    return (c0 < 0 || n > a.cap) ? -1 : pad_block((int)n, a);
+  };
   const int ept = (a.E + kWG - 1) / kWG;
   const int e0 = tid * ept;
+  if (a.counters) {
+    double part = 0.0;
+    for (int i = 0; i < ept; ++i)
+      if (e0 + i < a.E) {
+        const int p = padded(e0 + i);
+        part += p < 0 ? 1e18 : (double)p;
+      }
+    const int w = tid >> 6;
+    part = wave_sum_d(part);
+    if (lane_id() == 0) L.redd[w] = part;
+    __syncthreads();
+    double sum = 0.0;
+    for (int q = 0; q < kNW; ++q) sum += L.redd[q];
+    if (sum > (double)a.cap) {
+      if (tid == 0) *a.npp = -1;
+      return;
+    }
+  }
   int local = 0;
   for (int i = 0; i < ept; ++i)
-    if (e0 + i < a.E) local += pad_block(L.cnt[e0 + i], a);
+    if (e0 + i < a.E) local += padded(e0 + i);
   int pre = 0;
   {  // exclusive scan of the padded counts (wave scan, then across waves)
     const int w = tid >> 6;
@@ -1573,17 +1640,19 @@ __global__ __launch_bounds__(kWG) void k_ids_small(Args a) {
     const int e = e0 + i;
     if (e < a.E) {
       L.off[e] = pre;
-      pre += pad_block(L.cnt[e], a);
+      pre += padded(e);
     }
   }
   if (tid == kWG - 1) *a.npp = pre;
   __syncthreads();
   const int sentinel = a.M * a.k;
-  write_padding(a, a.E, L.off, [&](int e) { return L.cnt[e]; });
+  write_padding(a, a.E, L.off, [&](int e) { return c0_of(e) + L.cnt[e]; });
   for (int q = tid; q < sentinel; q += kWG) {
     const int r = L.rec[q];
-    if (r >= 0) a.sorted_ids[L.off[r & 0xFFFF] + (r >> 16)] = q;
+    if (r >= 0) a.sorted_ids[L.off[r & 0xFFFF] + c0_of(r & 0xFFFF) + (r >> 16)] = q;
   }
+  if (a.counters)
+    for (int e = tid; e < a.E; e += kWG) a.counters[e] = L.c0[e] + L.cnt[e];
 }
 
 __global__ void k_zero_npp(int32_t* npp) { *npp = 0; }
@@ -1668,7 +1737,7 @@ size_t workspace_of(int M, int E, int k) {
   if (M == 0) return 0;
   const int tw = choose_tw(M);
   const int64_t nwg = ((int64_t)M + tw - 1) / tw;
-  return kWsHeader + align16((size_t)2 * E * 4) + align16((size_t)nwg * E * 4) +
+  return kWsHeader + align16((size_t)3 * E * 4) + align16((size_t)nwg * E * 4) +
          align16((size_t)M * k * 4);
 }
 
@@ -1757,6 +1826,7 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_table_ready[kMaxDevices];
 std::mutex g_table_mu;
+const float* g_table_addr[kMaxDevices];  // the device's address of g_sig_table
 
 // Kernels that read the sigmoid table address it at LDS address 0, which
 // holds when they have no static LDS (their dynamic LDS then starts at 0).
@@ -1772,10 +1842,22 @@ bool no_static_lds(const void* fn) {
   return ok;
 }
 
-int ensure_sig_table(hipStream_t st) {
+int ensure_sig_table(hipStream_t st, const float** table) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRS_ERR_LAUNCH;
-  if (g_table_ready[dev].load(std::memory_order_acquire)) return MRS_OK;
+  if (g_table_ready[dev].load(std::memory_order_acquire)) {
+    *table = g_table_addr[dev];
+    return MRS_OK;
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    if (!g_table_addr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_sig_table)) != hipSuccess || !p) return MRS_ERR_LAUNCH;
+      g_table_addr[dev] = reinterpret_cast<const float*>(p);
+    }
+    *table = g_table_addr[dev];
+  }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cs) != hipSuccess) return MRS_ERR_LAUNCH;
   const void* fn = reinterpret_cast<const void*>(k_build_sig_table);
@@ -1945,7 +2027,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && !small_fits) return MRS_ERR_INVALID_ARG;
   if (want_small && !small_fits) return MRS_ERR_INVALID_ARG;  // cannot happen: the plan above fits
   if (a.tbl) {
-    const int rc = ensure_sig_table(st);
+    const int rc = ensure_sig_table(st, &a.sigtab);
     if (rc != MRS_OK) return rc;
   }
   if (want_small) {
@@ -1966,7 +2048,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace) + kWsHeader;
   a.ws_tot = reinterpret_cast<int32_t*>(ws);
   a.ws_pad = a.ws_tot + E;
-  ws += align16((size_t)2 * E * 4);
+  ws += align16((size_t)3 * E * 4);
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
@@ -2037,19 +2119,23 @@ int moe_route_sort_local(const void* logits, const float* bias, int M, int E, in
                          workspace_bytes, stream, 0u, nullptr, nullptr);
 }
 
-int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_t* sorted_ids,
-                      int32_t* expert_of_block, int32_t* num_post_pad, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+static int sort_from_ids_impl(const int32_t* ids, int M, int E, int k, int block, int32_t* counters,
+                              int64_t rows_capacity, int32_t* sorted_ids, int32_t* expert_of_block,
+                              int32_t* num_post_pad, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_sizes(M, E, k, block)) return MRS_ERR_INVALID_ARG;
-  if ((int64_t)M * k > INT32_MAX || max_rows_of(M, E, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if (counters && (rows_capacity < 0 || rows_capacity > (int64_t)INT32_MAX - (block - 1)))
+    return MRS_ERR_INVALID_ARG;
+  if ((int64_t)M * k > INT32_MAX || (!counters && max_rows_of(M, E, k, block) > INT32_MAX))
+    return MRS_ERR_OVERFLOW;
   if (num_post_pad == nullptr) return MRS_ERR_NULL_POINTER;
   if (!aligned(num_post_pad, 4)) return MRS_ERR_MISALIGNED;
+  if (counters && !aligned(counters, 4)) return MRS_ERR_MISALIGNED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (M == 0) {
+  if (M == 0 && !counters) {
     void* params[] = {&num_post_pad};
     return launch(reinterpret_cast<const void*>(k_zero_npp), 1, 1, 0, st, params, nullptr);
   }
-  if (!ids || !sorted_ids || !expert_of_block) return MRS_ERR_NULL_POINTER;
+  if ((M > 0 && !ids) || !sorted_ids || !expert_of_block) return MRS_ERR_NULL_POINTER;
   if (!aligned(ids, 4) || !aligned(sorted_ids, 4) || !aligned(expert_of_block, 4)) return MRS_ERR_MISALIGNED;
   Args a{};
   a.M = M;
@@ -2066,12 +2152,13 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
   a.sorted_ids = sorted_ids;
   a.eob = expert_of_block;
   a.npp = num_post_pad;
-  size_t oc, orc, oo, om, osc;
+  a.counters = counters;
+  a.cap = (int)(counters ? rows_capacity : 0);
   void* p_one[] = {&a};
   if (M <= kTwMax) {
     a.tw = M;
     a.nwg = 1;
-    const size_t lds = ids_lds_bytes(E, M, k, &oc, &orc, &oo, &om, &osc);
+    const size_t lds = ids_lds_plan(E, M, k).total;
     if (lds > kLdsLimit) return MRS_ERR_INVALID_ARG;
     return launch(reinterpret_cast<const void*>(k_ids_small), 1, kWG, lds, st, p_one, nullptr);
   }
@@ -2083,12 +2170,13 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace) + kWsHeader;
   a.ws_tot = reinterpret_cast<int32_t*>(ws);
   a.ws_pad = a.ws_tot + E;
-  ws += align16((size_t)2 * E * 4);
+  a.ws_c0 = a.ws_tot + 2 * E;
+  ws += align16((size_t)3 * E * 4);
   a.ws_hist = reinterpret_cast<int32_t*>(ws);
   ws += align16((size_t)a.nwg * E * 4);
   a.ws_slot = reinterpret_cast<int32_t*>(ws);
   a.fold = a.nwg <= kFoldRows ? 1 : 0;
-  const size_t lds_h = ids_lds_bytes(E, a.tw, k, &oc, &orc, &oo, &om, &osc);
+  const size_t lds_h = ids_lds_plan(E, a.tw, k).total;
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, 1, 0, 0, a.tw, k, 0).total;
   if (lds_h > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   int rc = launch(reinterpret_cast<const void*>(k_ids_hist), a.nwg, kWG, lds_h, st, p_one, nullptr);
@@ -2098,6 +2186,21 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
   return rc;
 }
 
+int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_t* sorted_ids,
+                      int32_t* expert_of_block, int32_t* num_post_pad, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return sort_from_ids_impl(ids, M, E, k, block, nullptr, 0, sorted_ids, expert_of_block, num_post_pad, workspace,
+                            workspace_bytes, stream);
+}
+
+int moe_sort_from_ids_counters(const int32_t* ids, int M, int E, int k, int block, int32_t* counters,
+                               int64_t rows_capacity, int32_t* sorted_ids, int32_t* expert_of_block,
+                               int32_t* num_post_pad, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!counters) return MRS_ERR_NULL_POINTER;
+  return sort_from_ids_impl(ids, M, E, k, block, counters, rows_capacity, sorted_ids, expert_of_block,
+                            num_post_pad, workspace, workspace_bytes, stream);
+}
+
 int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* out_single,
                                        float* out_pair, void* stream) {
   if (n < 0) return MRS_ERR_INVALID_ARG;
@@ -2105,7 +2208,8 @@ int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* 
   if (!bf16_bits || !out_single || !out_pair) return MRS_ERR_NULL_POINTER;
   if (!aligned(bf16_bits, 2) || !aligned(out_single, 4) || !aligned(out_pair, 4)) return MRS_ERR_MISALIGNED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int rc = ensure_sig_table(st);
+  const float* table = nullptr;
+  const int rc = ensure_sig_table(st, &table);
   if (rc != MRS_OK) return rc;
   void* params[] = {&bf16_bits, &n, &out_single, &out_pair};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_table_probe), dim3((n + 255) / 256),
