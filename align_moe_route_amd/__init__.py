@@ -35,6 +35,7 @@ EXPORTED = [
     "moe_route_sort_profiled",
     "moe_route_sort_local",
     "moe_sort_from_ids",
+    "moe_sort_from_ids_counters",
     "moe_route_sort_max_rows",
     "moe_route_sort_max_blocks",
     "moe_route_sort_workspace_bytes",
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_local.restype = i32
     L.moe_sort_from_ids.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_sort_from_ids.restype = i32
+    L.moe_sort_from_ids_counters.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, vp, sz, vp]
+    L.moe_sort_from_ids_counters.restype = i32
     for name in ("moe_route_sort_max_rows", "moe_route_sort_max_blocks"):
         getattr(L, name).argtypes = [i32, i32, i32, i32]
         getattr(L, name).restype = ctypes.c_int64
@@ -326,19 +329,37 @@ class SortOutput(NamedTuple):
 
 
 def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, workspace=None,
-                  stream=None) -> SortOutput:
+                  stream=None, counters=None, rows_capacity: Optional[int] = None) -> SortOutput:
     """The two sort phases from caller-given expert ids ([M, k] int32 GPU
-    tensor); ids outside [0, E) are dropped routes."""
+    tensor); ids outside [0, E) are dropped routes.
+
+    counters: optional int32 [E] GPU tensor of initial per-expert counters
+    (moe_sort_from_ids_counters): counters[e] rows at the head of expert e's
+    segment belong to the caller and are not written; the counters advance by
+    this call's routes.  rows_capacity (with counters): the sorted_ids entries
+    the call may use; by default the length of out.sorted_ids, required when
+    no out is given.  If a counter is negative or the rows do not fit,
+    num_post_pad reads -1 and nothing else is written."""
     import torch
     if not (isinstance(ids, torch.Tensor) and ids.is_cuda and ids.dtype == torch.int32 and ids.dim() == 2
             and ids.is_contiguous()):
         raise ValueError("ids must be a contiguous int32 [M, k] GPU tensor")
     M, k = ids.shape
     dev = ids.device
-    rows = max_rows(M, E, k, block)
-    blocks = max_blocks(M, E, k, block)
-    if rows < 0:
-        raise ValueError("invalid sizes or row capacity overflow")
+    if counters is not None:
+        _check_tensor(counters, dev, torch.int32, E, "counters")
+        if out is None:
+            if rows_capacity is None:
+                raise ValueError("rows_capacity is required with counters when no out is given")
+            rows, blocks = int(rows_capacity), int(rows_capacity) // block
+        else:
+            rows = int(out.sorted_ids.numel()) if rows_capacity is None else int(rows_capacity)
+            blocks = rows // block
+    else:
+        rows = max_rows(M, E, k, block)
+        blocks = max_blocks(M, E, k, block)
+        if rows < 0:
+            raise ValueError("invalid sizes or row capacity overflow")
     if out is None:
         out = SortOutput(torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
                          torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
@@ -354,9 +375,15 @@ def sort_from_ids(ids, E: int, block: int, *, out: Optional[SortOutput] = None, 
         _check_tensor(workspace, dev, None, 0, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
-                                     out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), ws_ptr,
-                                     ws_len, stream.cuda_stream))
+    if counters is not None:
+        rc = int(lib().moe_sort_from_ids_counters(ids.data_ptr() if M else None, M, E, k, block,
+                                                  counters.data_ptr(), rows, out.sorted_ids.data_ptr(),
+                                                  out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(),
+                                                  ws_ptr, ws_len, stream.cuda_stream))
+    else:
+        rc = int(lib().moe_sort_from_ids(ids.data_ptr(), M, E, k, block, out.sorted_ids.data_ptr(),
+                                         out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), ws_ptr,
+                                         ws_len, stream.cuda_stream))
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return out

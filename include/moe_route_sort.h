@@ -190,6 +190,45 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
                       int32_t* expert_of_block, int32_t* num_post_pad, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * moe_sort_from_ids_counters -- moe_sort_from_ids with caller-provided
+ * per-expert counters (page "gfx1250 ordinary-TP route optimization",
+ * Dispatch and contracts: caller-provided counters keep their initial
+ * offsets, and the counter and row capacity is the caller's obligation).
+ *
+ *   counters        int32[E] device array, read and written.  On entry
+ *                   counters[e] = c0[e] >= 0 is the number of rows the caller
+ *                   already holds at the head of expert e's segment.  With
+ *                   c[e] this call's routes to e (ids outside [0, E) dropped):
+ *                     count[e]  = c0[e] + c[e]
+ *                     padded[e] = ceil(count[e] / block) * block
+ *                     off[e]    = sum of padded[e'] for e' < e
+ *                     rows [off[e], off[e] + c0[e])  are not written (the
+ *                                                    caller's rows)
+ *                     sorted_ids[off[e] + c0[e] + r] = r-th slot routed to e in
+ *                                                    ascending slot order
+ *                     rows up to off[e] + padded[e]  = sentinel M*k
+ *                     expert_of_block as for moe_route_sort (every block)
+ *                     *num_post_pad = sum of padded[e]
+ *                   and on return counters[e] = count[e].
+ *   rows_capacity   entries of sorted_ids; expert_of_block must hold
+ *                   rows_capacity / block entries.  0 <= rows_capacity <=
+ *                   INT32_MAX - (block - 1), else MRS_ERR_INVALID_ARG.
+ *   M == 0 is allowed (ids may then be NULL): the segments hold the caller's
+ *   rows only.
+ * Device-side failure: when some c0[e] < 0 or the padded total exceeds
+ * rows_capacity, the call writes *num_post_pad = -1 and nothing else (the
+ * counters, sorted_ids and expert_of_block keep their contents).
+ * Counters are read before any of them is written, so the same array may be
+ * passed to consecutive calls (and captured in a graph); calls that may
+ * overlap in time need distinct counters and workspaces.  Everything else
+ * as for moe_sort_from_ids; counters == NULL returns MRS_ERR_NULL_POINTER.
+ */
+int moe_sort_from_ids_counters(const int32_t* ids, int M, int E, int k, int block, int32_t* counters,
+                               int64_t rows_capacity, int32_t* sorted_ids, int32_t* expert_of_block,
+                               int32_t* num_post_pad, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Capacity of sorted_ids: M*k + min(E, M*k)*(block-1), or -1 when the
  * arguments are invalid or the result does not fit int32. */
 int64_t moe_route_sort_max_rows(int M, int E, int k, int block);

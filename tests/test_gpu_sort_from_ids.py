@@ -157,3 +157,122 @@ def test_poisoned_tails_untouched():
     assert torch.all(out.sorted_ids[npp:] == poison)
     assert torch.all(out.expert_of_block[npp // block:] == poison)
     assert torch.equal(g, g0)
+
+
+# ---------------------------------------------------------------------------
+# Caller-provided initial counters (moe_sort_from_ids_counters).
+# ---------------------------------------------------------------------------
+POISON = -123456789
+
+
+def _run_counters(ids, E, block, c0, cap=None, out=None):
+    M, k = ids.shape
+    need = int(((c0 + np.bincount(ids[(ids >= 0) & (ids < E)].reshape(-1), minlength=E) + block - 1)
+                // block * block).sum())
+    cap = need + 3 * block if cap is None else cap
+    print(f"[gpu] sort_from_ids counters M={M} E={E} k={k} block={block} sum(c0)={int(c0.sum())} cap={cap}",
+          flush=True)
+    if out is None:
+        out = amr.SortOutput(torch.full((max(cap, 1),), POISON, dtype=torch.int32, device="cuda"),
+                             torch.full((max(cap // block, 1),), POISON, dtype=torch.int32, device="cuda"),
+                             torch.full((1,), POISON, dtype=torch.int32, device="cuda"))
+    cnt = torch.from_numpy(np.asarray(c0, dtype=np.int32)).cuda()
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    amr.sort_from_ids(ids_d, E, block, out=out, counters=cnt, rows_capacity=cap)
+    torch.cuda.synchronize()
+    return out, cnt, need, cap
+
+
+def _check_counters(ids, E, block, c0, out, cnt, cap):
+    ref = orc.sort_metadata_counters(ids, E, block, c0)
+    npp = int(out.num_post_pad.item())
+    rows = out.sorted_ids.cpu().numpy()
+    eob = out.expert_of_block.cpu().numpy()
+    assert npp == ref.meta.num_post_pad
+    w = ref.written
+    assert np.array_equal(rows[:npp][w], ref.meta.sorted_ids[w])
+    assert np.all(rows[:npp][~w] == POISON)          # the caller's rows are untouched
+    assert np.all(rows[npp:] == POISON)              # nothing past num_post_pad
+    assert np.array_equal(eob[:npp // block], ref.meta.expert_of_block)
+    assert np.all(eob[npp // block:] == POISON)
+    assert np.array_equal(cnt.cpu().numpy(), ref.counters_out)
+
+
+@pytest.mark.parametrize("M,E,k,block,maxc", [
+    (1, 896, 16, 32, 40), (4, 64, 4, 16, 5), (64, 896, 16, 128, 300), (65, 128, 8, 7, 20),
+    (150, 896, 16, 64, 200), (700, 896, 16, 64, 1), (5000, 896, 16, 128, 500), (9000, 512, 8, 128, 3),
+    (3000, 4096, 16, 128, 50), (2000, 1, 1, 3, 10)])
+def test_counters_nonzero_initial(M, E, k, block, maxc):
+    rng = np.random.default_rng(M * 3 + E)
+    ids = distinct_rows(rng, M, E, k, 0.8)
+    ids[rng.random(ids.shape) < 0.1] = -1
+    c0 = rng.integers(0, maxc + 1, E) * (rng.random(E) < 0.7)
+    out, cnt, _, cap = _run_counters(ids, E, block, c0)
+    _check_counters(ids, E, block, c0, out, cnt, cap)
+
+
+@pytest.mark.parametrize("M,E,k,block", [(8, 64, 4, 16), (500, 896, 16, 128), (0, 896, 16, 32)])
+def test_counters_all_dropped_and_empty(M, E, k, block):
+    rng = np.random.default_rng(M + 5)
+    ids = np.full((M, k), -1, np.int32)
+    c0 = rng.integers(0, 50, E)
+    out, cnt, _, cap = _run_counters(ids, E, block, c0)
+    _check_counters(ids, E, block, c0, out, cnt, cap)
+
+
+@pytest.mark.parametrize("M", [10, 100, 5000])
+def test_counters_fail_closed(M):
+    """A negative counter, or rows past the capacity: num_post_pad = -1 and
+    nothing else written (counters included)."""
+    E, k, block = 896, 16, 64
+    rng = np.random.default_rng(M)
+    ids = distinct_rows(rng, M, E, k)
+    c0 = rng.integers(0, 30, E)
+    for case in ("negative", "capacity"):
+        c = c0.copy()
+        if case == "negative":
+            c[E // 2] = -1
+            cap = None
+        else:
+            cap = int(((c + np.bincount(ids.reshape(-1), minlength=E) + block - 1) // block * block).sum()) - 1
+        out, cnt, _, cap = _run_counters(ids, E, block, c, cap=cap)
+        assert int(out.num_post_pad.item()) == -1, case
+        assert np.all(out.sorted_ids.cpu().numpy() == POISON), case
+        assert np.all(out.expert_of_block.cpu().numpy() == POISON), case
+        assert np.array_equal(cnt.cpu().numpy(), c), case
+
+
+@pytest.mark.parametrize("M", [40, 3000])
+def test_counters_graph_replay_with_changed_inputs(M):
+    """Eight replays of a captured call, each with new ids and new counters
+    written into the captured buffers; every replay checked."""
+    E, k, block = 896, 16, 64
+    rng = np.random.default_rng(M + 11)
+    cap = M * k + E * (block - 1) + E * 64 + block
+    out = amr.SortOutput(torch.full((cap,), POISON, dtype=torch.int32, device="cuda"),
+                         torch.full((cap // block,), POISON, dtype=torch.int32, device="cuda"),
+                         torch.full((1,), POISON, dtype=torch.int32, device="cuda"))
+    ids_d = torch.zeros((M, k), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((E,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # the stream's workspace, allocated outside the capture
+        amr.sort_from_ids(ids_d, E, block, out=out, counters=cnt, rows_capacity=cap, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        amr.sort_from_ids(ids_d, E, block, out=out, counters=cnt, rows_capacity=cap, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[gpu] graph replay M={M} E={E} x8", flush=True)
+    for rep in range(8):
+        ids = distinct_rows(rng, M, E, k, 0.5 * (rep % 3))
+        ids[rng.random(ids.shape) < 0.05 * (rep % 2)] = -1
+        c0 = rng.integers(0, 64, E)
+        out.sorted_ids.fill_(POISON)
+        out.expert_of_block.fill_(POISON)
+        ids_d.copy_(torch.from_numpy(ids))
+        cnt.copy_(torch.from_numpy(c0.astype(np.int32)))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        _check_counters(ids, E, block, c0, out, cnt, cap)

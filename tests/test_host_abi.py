@@ -173,6 +173,36 @@ def test_sort_from_ids_checks():
     assert ids_call(M=0, npp=None) == amr.MRS_ERR_NULL_POINTER
 
 
+def counters_call(**kw):
+    """moe_sort_from_ids_counters with fake aligned pointers (validation only)."""
+    L = amr.lib()
+    d = dict(ids=P, M=4, E=64, k=4, block=16, cnt=Q, cap=4096, rows=P, eob=P, npp=P, ws=None, ws_bytes=0)
+    d.update(kw)
+    return L.moe_sort_from_ids_counters(d["ids"], d["M"], d["E"], d["k"], d["block"], d["cnt"], d["cap"],
+                                        d["rows"], d["eob"], d["npp"], d["ws"], d["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(E=0), dict(E=4097), dict(k=0), dict(k=65), dict(block=0),
+                                dict(cap=-1), dict(cap=2 ** 31 - 1, block=16), dict(cap=2 ** 40)])
+def test_counters_invalid_arguments(kw):
+    assert counters_call(**kw) == amr.MRS_ERR_INVALID_ARG
+
+
+def test_counters_checks():
+    assert counters_call(cnt=None) == amr.MRS_ERR_NULL_POINTER
+    for name in ("ids", "rows", "eob", "npp"):
+        assert counters_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER
+    for name in ("ids", "rows", "eob", "npp", "cnt"):
+        assert counters_call(**{name: P + 2}) == amr.MRS_ERR_MISALIGNED
+    assert counters_call(M=1 << 26, k=64) == amr.MRS_ERR_OVERFLOW
+    need = amr.workspace_bytes(8192, 896, 16, 128)
+    assert counters_call(M=8192, E=896, k=16, block=128) == amr.MRS_ERR_WORKSPACE
+    assert counters_call(M=8192, E=896, k=16, block=128, ws=Q, ws_bytes=need - 4) == amr.MRS_ERR_WORKSPACE
+    # the largest legal capacity is accepted by the argument checks (the call
+    # then fails on the missing workspace, before any launch)
+    assert counters_call(M=8192, E=896, k=16, block=128, cap=2 ** 31 - 128) == amr.MRS_ERR_WORKSPACE
+
+
 def gemm_call(**kw):
     L = amr.lib()
     d = dict(x=P, w=P, sid=Q, eob=Q, npp=Q, M=64, k=8, E=64, K=256, N=256, block=64, y=P)
