@@ -193,8 +193,8 @@ int moe_sort_from_ids(const int32_t* ids, int M, int E, int k, int block, int32_
 /*
  * moe_sort_from_ids_counters -- moe_sort_from_ids with caller-provided
  * per-expert counters (page "gfx1250 ordinary-TP route optimization",
- * Dispatch and contracts: caller-provided counters keep their initial
- * offsets, and the counter and row capacity is the caller's obligation).
+ * Dispatch and contracts: counters the caller hands in start from the
+ * values it gave them, and sizing the counters and rows is up to the caller).
  *
  *   counters        int32[E] device array, read and written.  On entry
  *                   counters[e] = c0[e] >= 0 is the number of rows the caller

@@ -234,8 +234,8 @@ class CounterMeta:
 
 def sort_metadata_counters(ids: np.ndarray, E: int, block: int, initial: np.ndarray) -> CounterMeta:
     """The sort phases with caller-provided per-expert counters (page "gfx1250
-    ordinary-TP route optimization", Dispatch and contracts: caller-provided
-    counters keep their initial offsets).
+    ordinary-TP route optimization", Dispatch and contracts: counters that
+    the caller hands in start from the values it gave them).
 
     initial[e] >= 0 counts rows the caller already holds at the head of expert
     e's segment.  The segment then covers initial[e] + (this call's routes to
