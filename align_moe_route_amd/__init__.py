@@ -23,6 +23,7 @@ MRS_ERR_MISALIGNED = -3
 MRS_ERR_WORKSPACE = -4
 MRS_ERR_OVERFLOW = -5
 MRS_ERR_LAUNCH = -6
+MRS_ERR_SCRATCH = -7
 MRS_DTYPE_F32 = 0
 MRS_DTYPE_BF16 = 1
 FLAG_FORCE_SINGLE_WG = 1
@@ -34,6 +35,7 @@ EXPORTED = [
     "moe_route_sort_ex",
     "moe_route_sort_profiled",
     "moe_route_sort_local",
+    "moe_route_sort_static",
     "moe_sort_from_ids",
     "moe_sort_from_ids_counters",
     "moe_route_sort_max_rows",
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_sort_profiled.restype = i32
     L.moe_route_sort_local.argtypes = common[:8] + [i32, i32] + common[8:]
     L.moe_route_sort_local.restype = i32
+    L.moe_route_sort_static.argtypes = common[:14] + [vp]
+    L.moe_route_sort_static.restype = i32
     L.moe_sort_from_ids.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_sort_from_ids.restype = i32
     L.moe_sort_from_ids_counters.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, vp, sz, vp]
@@ -286,6 +290,47 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             raise RouteSortError(rc)
         return out, n.value
     rc = int(lib().moe_route_sort_ex(*args))
+    if rc != MRS_OK:
+        raise RouteSortError(rc)
+    return out
+
+
+def route_sort_static(logits, bias, k: int, n_group: int, topk_group: int, block: int, *,
+                      out: Optional[RouteSortOutput] = None, stream=None) -> RouteSortOutput:
+    """moe_route_sort_static: the route-sort path with the library's own
+    static scratch instead of a workspace (for callers that cannot allocate;
+    concurrent calls on one GPU race).  Arguments as for route_sort."""
+    import torch
+    if not (isinstance(logits, torch.Tensor) and logits.is_cuda and logits.dim() == 2 and logits.is_contiguous()):
+        raise ValueError("logits must be a contiguous [M, E] GPU tensor")
+    if logits.dtype == torch.float32:
+        dt = MRS_DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = MRS_DTYPE_BF16
+    else:
+        raise NotImplementedError(f"logits dtype {logits.dtype} (float32 or bfloat16 only)")
+    M, E = logits.shape
+    dev = logits.device
+    _check_tensor(bias, dev, torch.float32, E, "bias")
+    if bias.shape != (E,):
+        raise ValueError("bias must be a float32 [E] tensor")
+    rows, blocks = max_rows(M, E, k, block), max_blocks(M, E, k, block)
+    if rows < 0:
+        raise ValueError("invalid sizes or row capacity overflow")
+    if out is None:
+        out = RouteSortOutput(torch.empty((M, k), dtype=torch.int32, device=dev),
+                              torch.empty((M, k), dtype=torch.float32, device=dev),
+                              torch.empty((max(rows, 1),), dtype=torch.int32, device=dev),
+                              torch.empty((max(blocks, 1),), dtype=torch.int32, device=dev),
+                              torch.empty((1,), dtype=torch.int32, device=dev))
+    else:
+        _check_route_output(out, M, k, rows, blocks, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = int(lib().moe_route_sort_static(logits.data_ptr(), bias.data_ptr(), M, E, k, n_group, topk_group, block,
+                                         out.ids.data_ptr(), out.weights.data_ptr(), out.sorted_ids.data_ptr(),
+                                         out.expert_of_block.data_ptr(), out.num_post_pad.data_ptr(), dt,
+                                         stream.cuda_stream))
     if rc != MRS_OK:
         raise RouteSortError(rc)
     return out

@@ -1826,6 +1826,34 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_table_ready[kMaxDevices];
 std::mutex g_table_mu;
+
+// Scratch of moe_route_sort_static: the workspace of a call held in the
+// library's own device memory, one copy per GPU for the life of the process.
+// Host code never uses the array's name as an address: scratch_address()
+// asks the runtime for the current device's address once per device
+// (hipGetSymbolAddress) and every launch gets that pointer.  No call reads a
+// scratch word that it did not write earlier in the same call, so the array
+// needs no clearing; calls that overlap in time on one GPU share it and race.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRS_ERR_LAUNCH;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MRS_ERR_LAUNCH;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MRS_OK;
+}
 const float* g_table_addr[kMaxDevices];  // the device's address of g_sig_table
 
 // Kernels that read the sigmoid table address it at LDS address 0, which
@@ -1908,6 +1936,7 @@ const char* moe_route_sort_strerror(int code) {
     case MRS_ERR_WORKSPACE: return "workspace missing or too small";
     case MRS_ERR_OVERFLOW: return "M*k or the sorted-row capacity does not fit int32";
     case MRS_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MRS_ERR_SCRATCH: return "the call needs more scratch than moe_route_sort_static's 8 MiB";
     default: return "unknown error code";
   }
 }
@@ -2108,6 +2137,24 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
   return moe_route_sort_ex(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
                            sorted_ids, expert_of_block, num_post_pad, logits_dtype, workspace,
                            workspace_bytes, stream, 0u, nullptr);
+}
+
+int moe_route_sort_static(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                          int topk_group, int block, int32_t* out_ids, float* out_w, int32_t* sorted_ids,
+                          int32_t* expert_of_block, int32_t* num_post_pad, int logits_dtype, void* stream) {
+  const int rc = mrs_check_route_args(logits, bias, M, E, k, n_group, topk_group, block, out_ids, out_w,
+                                      sorted_ids, expert_of_block, num_post_pad, logits_dtype);
+  if (rc != MRS_OK) return rc;
+  if (max_rows_of(M, E, k, block) > INT32_MAX) return MRS_ERR_OVERFLOW;
+  if (workspace_of(M, E, k) > kStaticScratchBytes) return MRS_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (workspace_of(M, E, k) > 0) {
+    const int rs = scratch_address(&ws);
+    if (rs != MRS_OK) return rs;
+  }
+  return route_sort_impl(logits, bias, M, E, k, n_group, topk_group, block, 0, E, out_ids, out_w, sorted_ids,
+                         expert_of_block, num_post_pad, logits_dtype, ws, ws ? kStaticScratchBytes : 0, stream,
+                         0u, nullptr, nullptr);
 }
 
 int moe_route_sort_local(const void* logits, const float* bias, int M, int E, int k, int n_group,

@@ -60,7 +60,9 @@ enum {
                               /* not 4-byte aligned                             */
   MRS_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required     */
   MRS_ERR_OVERFLOW = -5,      /* M*k or the row capacity does not fit int32     */
-  MRS_ERR_LAUNCH = -6         /* the HIP runtime rejected a kernel launch       */
+  MRS_ERR_LAUNCH = -6,        /* the HIP runtime rejected a kernel launch       */
+  MRS_ERR_SCRATCH = -7        /* moe_route_sort_static: the call needs more     */
+                              /* scratch than the library's static 8 MiB        */
 };
 
 enum { MRS_DTYPE_F32 = 0, MRS_DTYPE_BF16 = 1 };
@@ -97,6 +99,28 @@ int moe_route_sort(const void* logits, const float* bias, int M, int E, int k, i
                    int topk_group, int block, int32_t* out_ids, float* out_w,
                    int32_t* sorted_ids, int32_t* expert_of_block, int32_t* num_post_pad,
                    int logits_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_sort_static -- moe_route_sort for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation) and so cannot provide a workspace.  The scratch is an
+ * 8 MiB array in the library's own device memory, one per GPU, held until
+ * the process ends; its address on the current device is looked up once per
+ * device, and the call itself allocates nothing.
+ *
+ *   Arguments, results and errors as for moe_route_sort, without workspace
+ *   and workspace_bytes.  Inputs whose moe_route_sort_workspace_bytes(M, E, k,
+ *   block) exceeds 8 MiB return MRS_ERR_SCRATCH before any launch (every
+ *   shape up to 16384 tokens x 4096 experts x top-16 fits; so does
+ *   65536 x 896 x top-16).
+ *   No call depends on what an earlier call left in the scratch.  All calls
+ *   on one GPU share the array: calls that may overlap in time (other
+ *   streams, other threads) race and give undefined results; serialise them
+ *   or use moe_route_sort with distinct workspaces.
+ */
+int moe_route_sort_static(const void* logits, const float* bias, int M, int E, int k, int n_group,
+                          int topk_group, int block, int32_t* out_ids, float* out_w, int32_t* sorted_ids,
+                          int32_t* expert_of_block, int32_t* num_post_pad, int logits_dtype, void* stream);
 
 /* Option bits for moe_route_sort_ex (path selection for tests and tuning;
  * every path computes the same result). */

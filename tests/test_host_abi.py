@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_strerror_names_every_code():
-    for c in range(-6, 1):
+    for c in range(-7, 1):
         s = amr.strerror(c)
         assert s and "unknown" not in s
     assert "unknown" in amr.strerror(-99)
@@ -171,6 +171,29 @@ def test_sort_from_ids_checks():
     assert ids_call(M=8192, E=896, k=16, block=128, ws=Q, ws_bytes=need - 4) == amr.MRS_ERR_WORKSPACE
     assert ids_call(M=8192, E=896, k=16, block=128, ws=Q + 4, ws_bytes=need + 64) == amr.MRS_ERR_MISALIGNED
     assert ids_call(M=0, npp=None) == amr.MRS_ERR_NULL_POINTER
+
+
+def static_call(M=4, E=64, k=4, n_group=8, topk_group=4, block=16, logits=P, bias=P, ids=P, w=P, rows=P,
+                eob=P, npp=P, dtype=0):
+    return amr.lib().moe_route_sort_static(logits, bias, M, E, k, n_group, topk_group, block, ids, w, rows, eob,
+                                           npp, dtype, None)
+
+
+def test_static_entry_checks():
+    """moe_route_sort_static validates like moe_route_sort and rejects shapes
+    whose scratch would exceed its 8 MiB before any launch."""
+    assert static_call(M=-1) == amr.MRS_ERR_INVALID_ARG
+    assert static_call(n_group=7) == amr.MRS_ERR_INVALID_ARG
+    assert static_call(dtype=3) == amr.MRS_ERR_INVALID_ARG
+    for name in ("logits", "bias", "ids", "w", "rows", "eob", "npp"):
+        assert static_call(**{name: None}) == amr.MRS_ERR_NULL_POINTER
+    assert static_call(logits=P + 4) == amr.MRS_ERR_MISALIGNED
+    big = dict(M=1 << 18, E=4096, k=16, n_group=16, topk_group=8, block=128)
+    assert amr.workspace_bytes(1 << 18, 4096, 16, 128) > 8 << 20
+    assert static_call(**big) == amr.MRS_ERR_SCRATCH
+    assert "8 MiB" in amr.strerror(amr.MRS_ERR_SCRATCH)
+    for M, E, k, blk in [(16384, 4096, 16, 128), (65536, 896, 16, 128), (8192, 896, 16, 128)]:
+        assert amr.workspace_bytes(M, E, k, blk) <= 8 << 20
 
 
 def counters_call(**kw):
