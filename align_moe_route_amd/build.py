@@ -21,7 +21,36 @@ FLAGS = [
 ]
 
 
+GEN_SRC = os.path.join(HERE, "csrc", "gen_sig_table.cpp")
+GEN_EXE = os.path.join(HERE, "csrc", "gen_sig_table")
+TABLE_INC = os.path.join(HERE, "csrc", "sig_table.inc")
+
+
+def _run(cmd, what):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if res.returncode != 0:
+        raise RuntimeError(f"{what} failed ({res.returncode}):\n{msg}")
+    return msg
+
+
+def build_table(verbose: bool = False) -> str:
+    """Generate sig_table.inc: the host program evaluates the library's own
+    correctly rounded sigmoid on every BF16 pattern the table covers."""
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=gfx950", "-O2", "-std=c++17", "-ffp-contract=off",
+           "-I", os.path.join(HERE, "csrc"), GEN_SRC, "-o", GEN_EXE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _run(cmd, "compiling the table generator")
+    _run([GEN_EXE, TABLE_INC + ".tmp"], "generating the sigmoid table")
+    os.replace(TABLE_INC + ".tmp", TABLE_INC)
+    os.remove(GEN_EXE)
+    return TABLE_INC
+
+
 def build(verbose: bool = False) -> str:
+    build_table(verbose)
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *SRCS,
            "-o", OUT + ".tmp"]
     if verbose:

@@ -76,6 +76,7 @@ constexpr int kSigBytes = kSigEntries * 4;
 constexpr uint32_t kSigBase = 0x3300;
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kWsHeader = 256;
+constexpr int kMaxDevices = 64;          // devices whose per-device host state is kept
 
 enum { KIND_SMALL = 0, KIND_SELECT = 1, KIND_SCATTER = 2 };
 enum { LOAD_VEC = 0, LOAD_STAGE = 1 };
@@ -268,9 +269,26 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 // rare inputs near an FP32 rounding midpoint settled in double-double).
 __device__ __forceinline__ float sigmoid_exact(float x) { return sigrn::sigmoid_rn32(x); }
 
-// The sigmoid table (built once per device by k_build_sig_table from
-// sigmoid_exact, copied into LDS offset 0 by every workgroup that uses it).
-__device__ __align__(16) float g_sig_table[kSigEntries];
+// The sigmoid table, generated at build time (gen_sig_table.cpp runs
+// sigmoid_rn32 on the host for every entry) and held in kSigCopies identical
+// copies: workgroup w copies copy (w >> 3) mod kSigCopies into LDS offset 0,
+// so the 32 workgroups that share an XCD's L2 (w mod 8 fixed) read 32
+// different copies instead of all requesting the same lines at once.
+#include "sig_table.inc"
+constexpr int kSigCopies = 32;
+#define SIG_ROW {SIG_TABLE_BITS}
+#define SIG_ROW4 SIG_ROW, SIG_ROW, SIG_ROW, SIG_ROW
+#define SIG_ROW16 SIG_ROW4, SIG_ROW4, SIG_ROW4, SIG_ROW4
+// Not const: an internal const array that no device code names would be
+// dropped from the code object, and the host looks it up by name.
+__device__ __align__(16) uint32_t g_sig_table[kSigCopies][kSigEntries] = {SIG_ROW16, SIG_ROW16};
+#undef SIG_ROW16
+#undef SIG_ROW4
+#undef SIG_ROW
+__device__ __forceinline__ const float* sig_table_copy(const float* base, int wg) {
+  return base + (size_t)((wg >> 3) & (kSigCopies - 1)) * kSigEntries;
+}
+
 
 // Byte offset of a BF16 pattern's entry: 8 * clamp(|h| - base, 0, 4095) + 4 * sign.
 __device__ __forceinline__ uint32_t sig_off1(uint32_t h) {
@@ -1022,7 +1040,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
   }
   if (a.tbl) {
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.sigtab);
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(sig_table_copy(a.sigtab, blockIdx.x));
 #pragma unroll
     for (int j = 0; j * kWG * 16 < kSigBytes; ++j)
       __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
@@ -1665,21 +1683,13 @@ __global__ __launch_bounds__(256) void k_sigmoid_probe(const float* x, int n, fl
   }
 }
 
-// Entry 2t + s of the table = correctly rounded sigmoid at BF16 pattern
-// (kSigBase + t) | s << 15.
-__global__ __launch_bounds__(256) void k_build_sig_table() {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j < kSigEntries) {
-    const uint32_t h = ((kSigBase + (uint32_t)(j >> 1)) & 0x7FFFu) | ((uint32_t)(j & 1) << 15);
-    g_sig_table[j] = sigmoid_exact(__uint_as_float(h << 16));
-  }
-}
-
 // Sigmoid of BF16 patterns through the LDS table, by the single-value (o1)
 // and the packed-pair (o2, pairing element i with i ^ 1) address forms.
-__global__ __launch_bounds__(256) void k_sigmoid_table_probe(const uint16_t* h, int n, float* o1, float* o2) {
+__global__ __launch_bounds__(256) void k_sigmoid_table_probe(const float* table, const uint16_t* h, int n, float* o1,
+                                                             float* o2) {
   float* tab = reinterpret_cast<float*>(g_lds);
-  for (int j = threadIdx.x; j < kSigEntries; j += 256) tab[j] = g_sig_table[j];
+  const float* src = sig_table_copy(table, blockIdx.x);
+  for (int j = threadIdx.x; j < kSigEntries; j += 256) tab[j] = src[j];
   __syncthreads();
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) {
@@ -1801,10 +1811,26 @@ struct Timing {
   int n;  // launches so far
 };
 
+// Raises a kernel's dynamic-LDS limit when a launch needs more than 64 KiB;
+// the largest value set so far per (kernel, device) is remembered, so the
+// runtime is asked once per kernel and device rather than on every launch.
+bool ensure_lds_limit(const void* fn, size_t lds) {
+  if (lds <= 64 * 1024) return true;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> set[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& cur = set[dev][fn];
+  if (cur >= lds) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return false;
+  cur = lds;
+  return true;
+}
+
 int launch(const void* fn, int grid, int block, size_t lds, hipStream_t stream, void** params, Timing* tm) {
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return MRS_ERR_LAUNCH;
+  if (!ensure_lds_limit(fn, lds)) return MRS_ERR_LAUNCH;
   hipError_t err;
   if (tm) {
     if (tm->n >= kMaxLaunches) return MRS_ERR_LAUNCH;
@@ -1819,13 +1845,19 @@ int launch(const void* fn, int grid, int block, size_t lds, hipStream_t stream, 
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// The sigmoid table is built once per device, on the first call that needs it:
-// launched on the caller's stream and waited for (the only host wait of the
-// library).  A first call made under stream capture puts the build into the
-// captured graph instead and leaves the device marked as not built.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_table_ready[kMaxDevices];
-std::mutex g_table_mu;
+// Kernels that read the sigmoid table address it at LDS address 0, which
+// holds when they have no static LDS (their dynamic LDS then starts at 0).
+bool no_static_lds(const void* fn) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, bool> known;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = known.find(fn);
+  if (it != known.end()) return it->second;
+  hipFuncAttributes attr{};
+  const bool ok = hipFuncGetAttributes(&attr, fn) == hipSuccess && attr.sharedSizeBytes == 0;
+  known.emplace(fn, ok);
+  return ok;
+}
 
 // Scratch of moe_route_sort_static: the workspace of a call held in the
 // library's own device memory, one copy per GPU for the life of the process.
@@ -1854,50 +1886,27 @@ int scratch_address(void** out) {
   *out = p;
   return MRS_OK;
 }
-const float* g_table_addr[kMaxDevices];  // the device's address of g_sig_table
 
-// Kernels that read the sigmoid table address it at LDS address 0, which
-// holds when they have no static LDS (their dynamic LDS then starts at 0).
-bool no_static_lds(const void* fn) {
-  static std::mutex mu;
-  static std::unordered_map<const void*, bool> known;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = known.find(fn);
-  if (it != known.end()) return it->second;
-  hipFuncAttributes attr{};
-  const bool ok = hipFuncGetAttributes(&attr, fn) == hipSuccess && attr.sharedSizeBytes == 0;
-  known.emplace(fn, ok);
-  return ok;
-}
+// The device address of the sigmoid table (looked up once per device; no
+// launch, no wait).
+std::atomic<const float*> g_table_addr[kMaxDevices];
+std::mutex g_table_mu;
 
-int ensure_sig_table(hipStream_t st, const float** table) {
+int sig_table_address(const float** table) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRS_ERR_LAUNCH;
-  if (g_table_ready[dev].load(std::memory_order_acquire)) {
-    *table = g_table_addr[dev];
-    return MRS_OK;
-  }
-  {
+  const float* t = g_table_addr[dev].load(std::memory_order_acquire);
+  if (!t) {
     std::lock_guard<std::mutex> lock(g_table_mu);
-    if (!g_table_addr[dev]) {
+    t = g_table_addr[dev].load(std::memory_order_relaxed);
+    if (!t) {
       void* p = nullptr;
-      if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_sig_table)) != hipSuccess || !p) return MRS_ERR_LAUNCH;
-      g_table_addr[dev] = reinterpret_cast<const float*>(p);
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_sig_table)) != hipSuccess || p == nullptr) return MRS_ERR_LAUNCH;
+      t = reinterpret_cast<const float*>(p);
+      g_table_addr[dev].store(t, std::memory_order_release);
     }
-    *table = g_table_addr[dev];
   }
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return MRS_ERR_LAUNCH;
-  const void* fn = reinterpret_cast<const void*>(k_build_sig_table);
-  if (cs != hipStreamCaptureStatusNone)
-    return hipLaunchKernel(fn, dim3(kSigEntries / 256), dim3(256), nullptr, 0, st) == hipSuccess ? MRS_OK
-                                                                                          : MRS_ERR_LAUNCH;
-  std::lock_guard<std::mutex> lock(g_table_mu);
-  if (g_table_ready[dev].load(std::memory_order_acquire)) return MRS_OK;
-  if (hipLaunchKernel(fn, dim3(kSigEntries / 256), dim3(256), nullptr, 0, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return MRS_ERR_LAUNCH;
-  g_table_ready[dev].store(1, std::memory_order_release);
+  *table = t;
   return MRS_OK;
 }
 
@@ -2056,7 +2065,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   if ((flags & MRS_FLAG_FORCE_SINGLE_WG) && !small_fits) return MRS_ERR_INVALID_ARG;
   if (want_small && !small_fits) return MRS_ERR_INVALID_ARG;  // cannot happen: the plan above fits
   if (a.tbl) {
-    const int rc = ensure_sig_table(st, &a.sigtab);
+    const int rc = sig_table_address(&a.sigtab);
     if (rc != MRS_OK) return rc;
   }
   if (want_small) {
@@ -2256,9 +2265,9 @@ int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* 
   if (!aligned(bf16_bits, 2) || !aligned(out_single, 4) || !aligned(out_pair, 4)) return MRS_ERR_MISALIGNED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const float* table = nullptr;
-  const int rc = ensure_sig_table(st, &table);
+  const int rc = sig_table_address(&table);
   if (rc != MRS_OK) return rc;
-  void* params[] = {&bf16_bits, &n, &out_single, &out_pair};
+  void* params[] = {&table, &bf16_bits, &n, &out_single, &out_pair};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_table_probe), dim3((n + 255) / 256),
                                          dim3(256), params, kSigBytes, st);
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;

@@ -33,11 +33,9 @@
  * device memory owned by the caller.  Inputs are never written.  Nothing
  * outside the defined ranges of the outputs is written.  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL = the default stream), never
- * allocate, and may be captured in a HIP graph.  The one host wait: the first
- * call with BF16 logits on a device builds a 32 KiB constant table (the
- * correctly rounded sigmoid of every BF16 value, in library-owned device
- * memory) on `stream` and waits for it; a first call made under stream
- * capture records that build into the graph instead.
+ * allocate, never wait on the host, and may be captured in a HIP graph.  BF16
+ * logits are scored through a constant table (the correctly rounded sigmoid
+ * of every BF16 value) that is part of the library's code object.
  *
  * Errors: a negative return code, detected before any launch; on error the
  * outputs are untouched.  moe_route_sort_strerror() names each code.
@@ -280,8 +278,8 @@ int moe_route_sort_sigmoid_probe(const float* x, int n, float* fast_out, float* 
  * Diagnostics: the correctly rounded sigmoid of BF16 logits as the kernels
  * read it from their LDS table, for n BF16 bit patterns (device uint16_t):
  * out_single[i] through the one-value address form, out_pair[i] through the
- * packed two-value form (element i paired with i ^ 1).  The first call on a
- * device builds the table (see moe_route_sort).  Asynchronous on stream.
+ * packed two-value form (element i paired with i ^ 1).  Asynchronous on
+ * stream.
  * Returns MRS_OK or an error code.
  */
 int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* out_single,
