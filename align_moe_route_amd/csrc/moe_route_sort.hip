@@ -709,8 +709,11 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
 // is redone with `exact` keys) and the candidate line is lowered by twice the
 // key error.  Written for a short instruction stream: compile-time layout,
 // table offsets with packed 16-bit arithmetic, straight-line group and
-// threshold stages.
-template <int SEG, int EPL, bool BF16, int MODE>
+// threshold stages.  LPG > 0 fixes the lanes per group at compile time (the
+// group stage then has no run-time branches or loop bounds); LPG == 0 reads
+// it from the arguments.  Maxima use v_med3 with +inf, which, unlike fmaxf,
+// needs no NaN-canonicalising copy of its operands (no key is NaN).
+template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act, int t, int tl,
                                           const unsigned char* stage, const float* bv, double delta,
                                           double epsg, bool exact) {
@@ -739,7 +742,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   auto put_key = [&](int i, float key) {
     av[i] = key;
     l2 = __builtin_amdgcn_fmed3f(lm, l2, key);  // second largest of {lm >= l2, key}
-    lm = fmaxf(lm, key);
+    lm = __builtin_amdgcn_fmed3f(lm, key, INFINITY);
   };
   auto put_pair = [&](int i, uint32_t d) {  // BF16 logits of experts i, i+1 packed in d
     uint32_t o0, o1;
@@ -849,28 +852,37 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   bool allowed = act;
   bool redo = false;
   if (a.gstage) {
+    constexpr int LG = LPG == 1 ? 0 : LPG == 2 ? 1 : LPG == 4 ? 2 : LPG == 8 ? 3 : LPG == 16 ? 4 : LPG == 32 ? 5 : -1;
+    static_assert(LPG == 0 || LG >= 0, "lanes per group: a power of two up to 32");
+    const int lg_lpg = LPG ? LG : a.lg_lpg;
+    const int ngs = LPG ? SEG / LPG : a.n_group;  // groups in a segment (n_group)
     float g1 = lm, g2 = l2;
 #pragma unroll
     for (int lev = 0; lev < (SEG == 64 ? 5 : 4); ++lev) {
-      if (lev < a.lg_lpg) {  // wave-uniform
+      if (lev < lg_lpg) {  // wave-uniform
         // merge two (largest, second largest) pairs: the new second largest is
         // the median of both largest values and the larger second value
         const float p1 = butterfly_partner(g1, lev);
         const float p2 = butterfly_partner(g2, lev);
-        g2 = __builtin_amdgcn_fmed3f(g1, p1, fmaxf(g2, p2));
-        g1 = fmaxf(g1, p1);
+        g2 = __builtin_amdgcn_fmed3f(g1, p1, __builtin_amdgcn_fmed3f(g2, p2, INFINITY));
+        g1 = __builtin_amdgcn_fmed3f(g1, p1, INFINITY);
       }
     }
     const uint32_t gsu = f2s(g1 + g2);
-    const int g = ls >> a.lg_lpg;
+    const int g = ls >> lg_lpg;
     const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
     unsigned long long* gc = L.gcomp + w * kWave + seg * SEG;
-    if ((ls & ((1 << a.lg_lpg) - 1)) == 0) gc[g] = cg;
+    if ((ls & ((1 << lg_lpg) - 1)) == 0) gc[g] = cg;
     wave_sync_lds();
     int rank = 0;
-    for (int h = 0; h < a.n_group; h += 2) {  // n_group is even here
-      const unsigned long long c0 = gc[h], c1 = gc[h + 1];
-      rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
+    if constexpr (LPG > 0) {
+#pragma unroll
+      for (int h = 0; h < SEG / LPG; ++h) rank += (gc[h] > cg ? 1 : 0);
+    } else {
+      for (int h = 0; h < ngs; h += 2) {  // n_group is even here
+        const unsigned long long c0 = gc[h], c1 = gc[h + 1];
+        rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
+      }
     }
     const bool keep = rank < a.topk_group;
     if (!exact) {
@@ -1020,7 +1032,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 // Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets
 // and the per-token expert lists in LDS.  Wave w, round it takes tokens
 // (it*kNW + w)*NSEG + segment.
-template <int SEG, int EPL, bool BF16, int MODE>
+template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
@@ -1128,10 +1140,10 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         }
       }
       const bool act = tl >= 0;
-      int st = lean_token<SEG, EPL, BF16, MODE>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
+      int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
       if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
         const bool redo = act && st == TOK_REDO_EXACT;
-        const int st2 = lean_token<SEG, EPL, BF16, MODE>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
+        const int st2 = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
         if (redo) st = st2;
       }
       if (act && st == TOK_ESCALATE && ls == 0) {
@@ -1231,10 +1243,10 @@ __device__ void write_padding(const Args& a, int n, const int* off, F cnt) {
 // Kernels.
 // ----------------------------------------------------------------------------
 // Everything in one workgroup (M <= 64): one launch per call.
-template <int SEG, int EPL, bool BF16, int MODE>
+template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
-  select_tokens<SEG, EPL, BF16, MODE>(a, L, 0, a.M);
+  select_tokens<SEG, EPL, BF16, MODE, LPG>(a, L, 0, a.M);
   const int tid = threadIdx.x;
   if (a.M == 1 && a.e_lo == 0 && a.EL == a.E) {
     // one token over all experts: its k picks are distinct and ascending, so
@@ -1267,13 +1279,13 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
 
 // Multi-workgroup path, launch 1: selection, per-workgroup histogram row and
 // one record (expert, rank inside the workgroup) per slot.
-template <int SEG, int EPL, bool BF16, int MODE>
+template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __global__ __launch_bounds__(kWG) void k_select(Args a) {
   const Lds L = carve(KIND_SELECT, a);
   const int w = blockIdx.x;
   const int t0 = w * a.tw;
   const int nt = min(a.tw, a.M - t0);
-  select_tokens<SEG, EPL, BF16, MODE>(a, L, t0, nt);
+  select_tokens<SEG, EPL, BF16, MODE, LPG>(a, L, t0, nt);
   // histogram row and slot records over experts [e_lo, e_lo + EL), numbered
   // from 0; a pick outside that range is recorded as a dropped route (-1)
   const unsigned long long* bits = L.bits + a.e_lo;
@@ -1802,6 +1814,18 @@ MRS_PICK(k_small)
 MRS_PICK(k_select)
 #undef MRS_PICK
 
+// Layouts compiled with the lanes per group fixed (group stage without run-time
+// branches): BF16 rows of 896 experts in 8 groups, as 32-lane segments of 28
+// experts per lane (batches) and as 64-lane segments of 14 (a few tokens).
+KernelFn pick_fixed_group(bool small, int seg, int epl, bool bf16, int mode, int lpg) {
+  if (!bf16 || mode != LOAD_STAGE) return nullptr;
+  if (seg == 32 && epl == 28 && lpg == 4)
+    return small ? k_small<32, 28, true, LOAD_STAGE, 4> : k_select<32, 28, true, LOAD_STAGE, 4>;
+  if (seg == 64 && epl == 14 && lpg == 8)
+    return small ? k_small<64, 14, true, LOAD_STAGE, 8> : k_select<64, 14, true, LOAD_STAGE, 8>;
+  return nullptr;
+}
+
 // Optional HIP events of one call (diagnostics): launch i is made with
 // hipExtLaunchKernel, which stamps ev[2i] and ev[2i+1] with the start and end
 // of that kernel's own execution.
@@ -2074,7 +2098,9 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.rows_first = 1;
     const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
     void* params[] = {&a};
-    const void* fn = reinterpret_cast<const void*>(pick_k_small(a.seg, a.epl, bf16, mode));
+    KernelFn kf = a.gstage ? pick_fixed_group(true, a.seg, a.epl, bf16, mode, a.seg / n_group) : nullptr;
+    if (!kf) kf = pick_k_small(a.seg, a.epl, bf16, mode);
+    const void* fn = reinterpret_cast<const void*>(kf);
     if (a.tbl && !no_static_lds(fn)) return MRS_ERR_LAUNCH;
     return launch(fn, 1, kWG, lds, st, params, tm);
   }
@@ -2095,7 +2121,9 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
   const size_t lds_sct = lds_plan(KIND_SCATTER, E, n_group, a.gstage, 0, a.tw, k, 0).total;
   if (lds_sel > kLdsLimit || lds_sct > kLdsLimit) return MRS_ERR_INVALID_ARG;
   void* p_one[] = {&a};
-  const void* fsel = reinterpret_cast<const void*>(pick_k_select(a.seg, a.epl, bf16, mode));
+  KernelFn ks = a.gstage ? pick_fixed_group(false, a.seg, a.epl, bf16, mode, a.seg / n_group) : nullptr;
+  if (!ks) ks = pick_k_select(a.seg, a.epl, bf16, mode);
+  const void* fsel = reinterpret_cast<const void*>(ks);
   if (a.tbl && !no_static_lds(fsel)) return MRS_ERR_LAUNCH;
   int rc = launch(fsel, a.nwg, kWG, lds_sel, st, p_one, tm);
   // the sort phases see only the experts that get metadata
