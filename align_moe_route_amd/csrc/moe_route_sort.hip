@@ -268,6 +268,17 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 // Correctly rounded FP32 sigmoid (sigmoid_rn.h: float64 quotient, with the
 // rare inputs near an FP32 rounding midpoint settled in double-double).
 __device__ __forceinline__ float sigmoid_exact(float x) { return sigrn::sigmoid_rn32(x); }
+// The same with the double-double settlement as a call (reached about once in
+// 2^19 evaluations), for code that keeps many registers live around it.
+__device__ __attribute__((noinline)) float sigmoid_settle(float x, float dn, float up) {
+  return sigrn::rn32_resolve((double)x, dn, up);
+}
+__device__ __forceinline__ float sigmoid_exact_lean(float x) {
+  bool amb;
+  float up;
+  const float dn = sigrn::sigmoid_rn32_try(x, amb, up);
+  return amb ? sigmoid_settle(x, dn, up) : dn;
+}
 
 // The sigmoid table, generated at build time (gen_sig_table.cpp runs
 // sigmoid_rn32 on the host for every entry) and held in kSigCopies identical
@@ -713,13 +724,47 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
 // group stage then has no run-time branches or loop bounds); LPG == 0 reads
 // it from the arguments.  Maxima use v_med3 with +inf, which, unlike fmaxf,
 // needs no NaN-canonicalising copy of its operands (no key is NaN).
+//
+// Long FP32 rows read as vectors (more than 32 experts per lane, 64-lane
+// segments) are loaded straight into the key registers `av`, and each key
+// replaces its logit there, so no staging registers are needed.  Once the
+// candidates are known the keys are dead: the wave then requests the first
+// half of its next token's row (`next_t`) into `av`, after the candidates'
+// own logits, so that the transfer overlaps the ranking and output steps and
+// the next token starts on data already in flight (`have_row`; it requests
+// the second half itself).  A token to be redone with exact keys is redone
+// after the wave's last token, by a pass that loads its whole row again.
+template <int SEG, int EPL, bool BF16, int MODE>
+constexpr bool row_in_keys() {
+  return !BF16 && MODE == LOAD_VEC && SEG == 64 && (EPL == 0 || EPL > 32);
+}
+
+// Requests vectors [Q0, Q1) of the lane's run of row `row` into v: slot 4q+j
+// holds expert own.expert(4q+j) (a load past the lane's run repeats its last
+// vector).
+template <int EPLM, int Q0, int Q1>
+__device__ __forceinline__ void load_row_vec(const Args& a, size_t row, int e_slot0, int vs, int nq,
+                                             float (&v)[EPLM]) {
+  const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.logits) + row + e_slot0);
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) {
+    const float4 x = src[(size_t)min(q, nq - 1) * vs];
+    v[4 * q + 0] = x.x;
+    v[4 * q + 1] = x.y;
+    v[4 * q + 2] = x.z;
+    v[4 * q + 3] = x.w;
+  }
+}
+
 template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act, int t, int tl,
                                           const unsigned char* stage, const float* bv, double delta,
-                                          double epsg, bool exact) {
+                                          double epsg, bool exact, float (&av)[EPL > 0 ? EPL : 64],
+                                          bool have_row, int next_t) {
   if (BF16) exact = true;
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
+  constexpr bool RIK = row_in_keys<SEG, EPL, BF16, MODE>();
   using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
@@ -736,7 +781,6 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const unsigned long long seg1 = NSEG == 1 ? 0ull : 0xFFFFFFFF00000000ull;
 
   // ---- 1. keys and lane top-2 ----
-  float av[EPLM];
   float lm = -INFINITY, l2 = -INFINITY;
   auto bias_of = [&](int i) { return (EPLM <= kBiasRegMax) ? bv[i] : L.biasT[i * SEG + ls]; };
   auto put_key = [&](int i, float key) {
@@ -767,11 +811,26 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     put_key(i, s + bias_of(i));
     if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
   };
-  if (EPL == 0) {  // slots past epl stay defined (their candidate bits are masked off)
+  if (EPL == 0 && !RIK) {  // slots past epl stay defined (their candidate bits are masked off)
 #pragma unroll
     for (int i = 0; i < EPLM; ++i) av[i] = 0.0f;
   }
-  {  // an idle segment's buffer holds a valid row too (row 0), so no branch here
+  if constexpr (RIK) {
+    // slots past epl hold a copy of the last vector; their bits are masked off
+    // the first half of the run may already be in flight (requested during
+    // the previous token); the second half is requested here
+    if (!have_row) load_row_vec<EPLM, 0, EPLM / 8>(a, row, own.e_slot0, ilw, epl / 4, av);
+    load_row_vec<EPLM, EPLM / 8, EPLM / 4>(a, row, own.e_slot0, ilw, epl / 4, av);
+#pragma unroll
+    for (int q = 0; q < EPLM / 4; ++q) {
+      if (EPL > 0 || 4 * q < epl) {  // wave-uniform
+        put(4 * q + 0, av[4 * q + 0]);
+        put(4 * q + 1, av[4 * q + 1]);
+        put(4 * q + 2, av[4 * q + 2]);
+        put(4 * q + 3, av[4 * q + 3]);
+      }
+    }
+  } else {  // an idle segment's buffer holds a valid row too (row 0), so no branch here
     if constexpr (MODE == LOAD_STAGE && !BF16) {
       const float* s32 = reinterpret_cast<const float*>(stage) + e0;
 #pragma unroll
@@ -976,7 +1035,26 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const int ce = has ? ci[ls] : 0;
   float sf = 0.0f;
   unsigned long long mykey = 0ull;  // below every real key
-  if (has) {
+  if constexpr (RIK) {
+    // The candidate's score is settled before the next row is requested, and
+    // the request is made on every path (a wave with no next row reads one
+    // 16-byte vector 16 times), so the compiler's in-order load accounting
+    // never makes a later wait cover that row.
+    const float x = reinterpret_cast<const float*>(a.logits)[row + (has ? ce : 0)];
+    bool amb;
+    float up;
+    sf = sigrn::sigmoid_rn32_try(x, amb, up);
+    if (__ballot(has && amb)) {
+      if (has && amb) sf = sigmoid_settle(x, sf, up);
+    }
+    const bool pf = next_t >= 0;  // wave-uniform
+    __builtin_amdgcn_sched_barrier(0);
+    load_row_vec<EPLM, 0, EPLM / 8>(a, pf ? (size_t)next_t * a.E : row, pf ? own.e_slot0 : 0, pf ? ilw : 0, epl / 4,
+                                    av);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has) mykey = ((unsigned long long)f2s(sf + L.bias[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
+    else sf = 0.0f;
+  } else if (has) {
     if constexpr (BF16) {
       uint32_t h;
       if constexpr (MODE == LOAD_STAGE) h = reinterpret_cast<const uint16_t*>(stage)[ce];
@@ -1102,6 +1180,13 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     constexpr bool IL = SEG == 64 && !BF16 && MODE == LOAD_VEC;
     const int ilw = IL ? a.ilw : 1;
     const Ownership own(ls, epl, ilw);
+    constexpr bool RIK = row_in_keys<SEG, EPL, BF16, MODE>();
+    float av[EPLM];  // keys of the wave's token (with RIK also its row, in flight)
+    if (RIK && w * NSEG < nt) {
+      // the first row overlaps the bias set-up below (its wait comes with the first key)
+      const int tl = tok_of(0);
+      load_row_vec<EPLM, 0, EPLM / 8>(a, (size_t)(t0 + tl) * a.E, own.e_slot0, ilw, epl / 4, av);
+    }
     float bv[EPLM <= kBiasRegMax ? EPLM : 1];
     float bmax = 0.0f;
     if constexpr (EPLM <= kBiasRegMax) {
@@ -1127,8 +1212,10 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     const double B = 1.0 + (double)__uint_as_float(wave_max_u32(__float_as_uint(bmax))) + 0x1p-20;
     const double delta = 0x1p-21 + (B + 1.0) * 0x1p-23;
     const double epsg = 2.0 * delta + (2.0 * B + 1.0) * 0x1p-23;
+    unsigned long long redo_rounds = 0;  // rounds whose token is redone with exact keys (RIK)
     for (int it = 0; (it * kNW + w) * NSEG < nt; ++it) {
       const int tl = tok_of(it);
+      const int tn = ((it + 1) * kNW + w) * NSEG < nt ? t0 + tok_of(it + 1) : -1;
       const int cb = a.nbuf > 1 ? (it & 1) : 0;
       const unsigned char* cur = stg + (size_t)(cb * NSEG + seg) * sb;
       if (MODE == LOAD_STAGE) {
@@ -1140,13 +1227,30 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         }
       }
       const bool act = tl >= 0;
-      int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false);
-      if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
+      int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false, av, RIK, tn);
+      if (RIK) {
+        // one token per wave: a token to redo is only noted here, and redone
+        // after the loop, so the exact pass does not share the loop's registers
+        if (__ballot(act && st == TOK_REDO_EXACT)) redo_rounds |= 1ull << it;
+        st = st == TOK_REDO_EXACT ? TOK_DONE : st;
+      } else if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
         const bool redo = act && st == TOK_REDO_EXACT;
-        const int st2 = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true);
+        const int st2 =
+            lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true, av, false, tn);
         if (redo) st = st2;
       }
       if (act && st == TOK_ESCALATE && ls == 0) {
+        const int q = atomicAdd(&L.misc[0], 1);
+        L.esc[q] = tl;
+      }
+    }
+    while (RIK && redo_rounds) {  // wave-uniform
+      const int it = __builtin_ctzll(redo_rounds);
+      redo_rounds &= redo_rounds - 1;
+      const int tl = tok_of(it);
+      const int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, true, t0 + tl, tl, stg, bv, delta, epsg, true, av,
+                                                           false, -1);
+      if (st == TOK_ESCALATE && ls == 0) {
         const int q = atomicAdd(&L.misc[0], 1);
         L.esc[q] = tl;
       }
