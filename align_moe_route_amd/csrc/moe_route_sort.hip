@@ -268,16 +268,10 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 // Correctly rounded FP32 sigmoid (sigmoid_rn.h: float64 quotient, with the
 // rare inputs near an FP32 rounding midpoint settled in double-double).
 __device__ __forceinline__ float sigmoid_exact(float x) { return sigrn::sigmoid_rn32(x); }
-// The same with the double-double settlement as a call (reached about once in
-// 2^19 evaluations), for code that keeps many registers live around it.
+// The double-double settlement as a call (reached about once in 2^19
+// evaluations), for code that keeps many registers live around it.
 __device__ __attribute__((noinline)) float sigmoid_settle(float x, float dn, float up) {
   return sigrn::rn32_resolve((double)x, dn, up);
-}
-__device__ __forceinline__ float sigmoid_exact_lean(float x) {
-  bool amb;
-  float up;
-  const float dn = sigrn::sigmoid_rn32_try(x, amb, up);
-  return amb ? sigmoid_settle(x, dn, up) : dn;
 }
 
 // The sigmoid table, generated at build time (gen_sig_table.cpp runs
@@ -329,6 +323,9 @@ __device__ __forceinline__ float sig_lds(uint32_t off) { return *reinterpret_cas
 // Wave-level helpers (wave64, DPP row shifts and broadcasts).
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+// The wave's index in its workgroup, in a scalar register (addresses derived
+// from it then need no vector registers).
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
@@ -767,7 +764,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   constexpr bool RIK = row_in_keys<SEG, EPL, BF16, MODE>();
   using MaskT = typename std::conditional<(EPLM > 32), unsigned long long, uint32_t>::type;
   const int lane = lane_id();
-  const int w = threadIdx.x >> 6;
+  const int w = wave_index();
   const int seg = NSEG == 1 ? 0 : (lane >> 5);
   const int ls = lane & (SEG - 1);
   const int epl = EPL > 0 ? EPL : a.epl;
@@ -821,6 +818,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     // the previous token); the second half is requested here
     if (!have_row) load_row_vec<EPLM, 0, EPLM / 8>(a, row, own.e_slot0, ilw, epl / 4, av);
     load_row_vec<EPLM, EPLM / 8, EPLM / 4>(a, row, own.e_slot0, ilw, epl / 4, av);
+    __builtin_amdgcn_sched_barrier(0);  // every request is out before the first key waits
 #pragma unroll
     for (int q = 0; q < EPLM / 4; ++q) {
       if (EPL > 0 || 4 * q < epl) {  // wave-uniform
@@ -1083,7 +1081,8 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 
   // ---- 6. outputs in expert order; weights s / sum(s), the sum in float64 ----
   const unsigned long long sb = __ballot(sel) & (NSEG == 1 ? ~0ull : (seg ? seg1 : ~seg1));
-  int pos = (int)__popcll(sb & ((1ull << lane) - 1ull));
+  // picks in lower lanes (mbcnt: no lane mask held in registers)
+  int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sb, 0u));
   if (IL && ilw > 1) {
     // candidates were compacted in lane order, which is not expert order here:
     // a pick's position is the number of picks with a smaller expert id
@@ -1115,7 +1114,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = wave_index();
   const int seg = lane_id() / SEG;
   const int ls = lane_id() % SEG;
   const int sb = a.stage_bytes;
@@ -1872,10 +1871,11 @@ typedef void (*KernelFn)(Args);
 // Experts per lane compiled as constants (straight-line code).  With 64-lane
 // segments any other value runs the variant that reads it at run time; 32-lane
 // segments are used only for the listed values.  FP32 rows with 64 experts per
-// lane also take the run-time variant: the constant one needs more registers
-// than a lane has at 16 waves per compute unit and measured slower.  A lane run that is a whole
-// number of 16-byte vectors loads straight from HBM (LOAD_VEC), otherwise the
-// rows go through the wave's LDS staging buffers (LOAD_STAGE).
+// lane also take the run-time variant: the constant one issues fewer
+// instructions but measured slower on the 16384 x 4096 workload (k_select
+// 72.5 against 68.9 us).  A lane run that is a whole number of 16-byte vectors
+// loads straight from HBM (LOAD_VEC), otherwise the rows go through the wave's
+// LDS staging buffers (LOAD_STAGE).
 constexpr bool vec_mode(int epl, bool bf16) { return (epl * (bf16 ? 2 : 4)) % 16 == 0; }
 bool seg32_epl(int epl) {
   return epl == 2 || epl == 4 || epl == 8 || epl == 16 || epl == 28 || epl == 32;
