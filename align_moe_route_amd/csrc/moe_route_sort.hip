@@ -66,6 +66,7 @@ constexpr int kNW = 16;                  // waves per workgroup
 constexpr int kWG = kNW * kWave;         // threads per workgroup, all kernels
 constexpr int kTwMax = 64;               // tokens per workgroup: one bit each in a 64-bit word
 constexpr int kEMax = 4096;              // 16 KiB of 32-bit counters, the pages' LDS bound
+constexpr int kKeysPreMax = 2048;        // small batches with at most this many keys precompute them
 constexpr int kBiasRegMax = 32;          // lanes keep their biases in registers up to this many experts
 // Correctly rounded sigmoid of every BF16 value, 8192 FP32 entries: entry
 // 2t + s is the value at the BF16 pattern (0x3300 + t) | s << 15.  Below the
@@ -79,7 +80,9 @@ constexpr size_t kWsHeader = 256;
 constexpr int kMaxDevices = 64;          // devices whose per-device host state is kept
 
 enum { KIND_SMALL = 0, KIND_SELECT = 1, KIND_SCATTER = 2 };
-enum { LOAD_VEC = 0, LOAD_STAGE = 1 };
+// LOAD_KEYS: the whole workgroup computes every exact key (and score) of the
+// batch into LDS first; the waves then select from them (small batches)
+enum { LOAD_VEC = 0, LOAD_STAGE = 1, LOAD_KEYS = 2 };
 enum { TOK_DONE = 0, TOK_REDO_EXACT = 1, TOK_ESCALATE = 2 };
 
 struct Args {
@@ -104,6 +107,7 @@ struct Args {
   int bias_dma;  // bias is copied into LDS by DMA (16-byte aligned, E % 4 == 0)
   int rows_first;  // issue the row copies before the shared data (latency-bound calls)
   int gstage;  // the group stage changes the result (1 < topk_group < n_group, G > 1)
+  int keys_pre;  // LOAD_KEYS: token tl's keys at stage + tl*stage_bytes, its scores E floats later
   int32_t* out_ids;
   float* out_w;
   int32_t* sorted_ids;
@@ -133,7 +137,8 @@ struct LdsPlan {
   size_t sig, bits, redd, off, cpre, ids, bias, biasT, cand_i, cand_c, gcomp, u, stage, ukey, grp, esc, misc, red, scan, total;
 };
 
-__host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes) {
+__host__ __device__ inline size_t stage_total(int fast, int seg, int nbuf, int stage_bytes, int key_rows = 0) {
+  if (key_rows > 0) return (size_t)key_rows * stage_bytes;  // LOAD_KEYS: one row per token
   return fast ? (size_t)kNW * nbuf * (kWave / seg) * stage_bytes : 0;
 }
 
@@ -194,7 +199,8 @@ struct Lds {
 extern __shared__ __align__(16) unsigned char g_lds[];
 
 __device__ inline Lds carve(int kind, const Args& a) {
-  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage, stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes),
+  const LdsPlan p = lds_plan(kind, a.E, a.n_group, a.gstage,
+                             stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes, a.keys_pre ? a.tw : 0),
                              a.tw, a.k, a.tbl);
   Lds L;
   L.bits = reinterpret_cast<unsigned long long*>(g_lds + p.bits);
@@ -758,7 +764,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
                                           const unsigned char* stage, const float* bv, double delta,
                                           double epsg, bool exact, float (&av)[EPL > 0 ? EPL : 64],
                                           bool have_row, int next_t) {
-  if (BF16) exact = true;
+  if (BF16 || MODE == LOAD_KEYS) exact = true;
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
   constexpr bool RIK = row_in_keys<SEG, EPL, BF16, MODE>();
@@ -812,7 +818,12 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 #pragma unroll
     for (int i = 0; i < EPLM; ++i) av[i] = 0.0f;
   }
-  if constexpr (RIK) {
+  if constexpr (MODE == LOAD_KEYS) {  // exact keys of this token, in expert order
+    const float* kr = reinterpret_cast<const float*>(stage) + e0;
+#pragma unroll
+    for (int i = 0; i < EPLM; ++i)
+      if (EPL > 0 || i < epl) put_key(i, kr[i]);
+  } else if constexpr (RIK) {
     // slots past epl hold a copy of the last vector; their bits are masked off
     // the first half of the run may already be in flight (requested during
     // the previous token); the second half is requested here
@@ -994,7 +1005,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   float thr = s2f(T);
   if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
   const bool ok = (NSEG == 1 || seg == 0) ? okseg[0] : okseg[NSEG - 1];
-  const bool amb_seg = exact && !BF16 && seg_max_u32<SEG>(f2s(lm)) == f2s(INFINITY);
+  const bool amb_seg = exact && !BF16 && MODE != LOAD_KEYS && seg_max_u32<SEG>(f2s(lm)) == f2s(INFINITY);
   int status = !act ? TOK_ESCALATE : ((!ok || amb_seg) ? TOK_ESCALATE : (redo ? TOK_REDO_EXACT : TOK_DONE));
 
   // ---- 4. candidates (keys >= thr), compacted in expert order ----
@@ -1033,7 +1044,13 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const int ce = has ? ci[ls] : 0;
   float sf = 0.0f;
   unsigned long long mykey = 0ull;  // below every real key
-  if constexpr (RIK) {
+  if constexpr (MODE == LOAD_KEYS) {
+    if (has) {
+      const float* kr = reinterpret_cast<const float*>(stage);
+      sf = kr[a.E + ce];
+      mykey = ((unsigned long long)f2s(kr[ce]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ce);
+    }
+  } else if constexpr (RIK) {
     // The candidate's score is settled before the next row is requested, and
     // the request is made on every path (a wave with no next row reads one
     // 16-byte vector 16 times), so the compiler's in-order load accounting
@@ -1161,6 +1178,25 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     if (!a.bias_dma) L.bias[e] = a.bias[e];
   }
   if (tid == 0) L.misc[0] = 0;
+  if constexpr (MODE == LOAD_KEYS) {
+    // every exact key and score of the batch, one (token, expert) per thread
+    // and pass: RN32 sigmoid (float64 quotient, double-double when it lies
+    // near a rounding midpoint) plus the bias
+    const int row_f = a.stage_bytes / 4;  // floats per token: E keys, then E scores
+    float* kf = reinterpret_cast<float*>(L.stage);
+    for (int e = tid; e < a.E; e += kWG) {
+      const float b = a.bias[e];  // requested together with the first logit
+      for (int tl = 0; tl < nt; ++tl) {
+        const float x = load_logit<BF16>(a.logits, (size_t)(t0 + tl) * a.E + e);
+        bool amb;
+        float up;
+        float sc = sigrn::sigmoid_rn32_try(x, amb, up);
+        if (amb) sc = sigmoid_settle(x, sc, up);
+        kf[tl * row_f + e] = sc + b;
+        kf[tl * row_f + a.E + e] = sc;
+      }
+    }
+  }
   if (a.tbl || a.bias_dma) {
     // loads complete in order: with R row copies issued after the shared
     // data, vmcnt <= R means the table and bias copies of this wave are done
@@ -1186,9 +1222,11 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
       const int tl = tok_of(0);
       load_row_vec<EPLM, 0, EPLM / 8>(a, (size_t)(t0 + tl) * a.E, own.e_slot0, ilw, epl / 4, av);
     }
-    float bv[EPLM <= kBiasRegMax ? EPLM : 1];
+    float bv[EPLM <= kBiasRegMax ? EPLM : 1] = {};
     float bmax = 0.0f;
-    if constexpr (EPLM <= kBiasRegMax) {
+    if constexpr (MODE == LOAD_KEYS) {
+      // the keys are complete and exact: no biases or error bounds are needed
+    } else if constexpr (EPLM <= kBiasRegMax) {
 #pragma unroll
       for (int i = 0; i < EPLM; ++i) {
         bv[i] = i < epl ? L.bias[own.expert(i)] : 0.0f;
@@ -1349,19 +1387,23 @@ __device__ void write_padding(const Args& a, int n, const int* off, F cnt) {
 template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
-  select_tokens<SEG, EPL, BF16, MODE, LPG>(a, L, 0, a.M);
   const int tid = threadIdx.x;
-  if (a.M == 1 && a.e_lo == 0 && a.EL == a.E) {
+  const bool one = a.M == 1 && a.e_lo == 0 && a.EL == a.E;
+  if (one) {
     // one token over all experts: its k picks are distinct and ascending, so
     // pick j owns rows [j*block, (j+1)*block) -- its slot j, then sentinels
-    // (M*k = k) -- and block j; no scan over the experts is needed
+    // (M*k = k) -- and block j; no scan over the experts is needed, and only
+    // the block's expert depends on the selection
     const int rows = a.k * a.block;
     for (int r = tid; r < rows; r += kWG) {
       const int j = div_block(r, a);
       a.sorted_ids[r] = r == j * a.block ? j : a.k;
     }
-    for (int j = tid; j < a.k; j += kWG) a.eob[j] = L.ids[j];
     if (tid == 0) *a.npp = rows;
+  }
+  select_tokens<SEG, EPL, BF16, MODE, LPG>(a, L, 0, a.M);
+  if (one) {
+    for (int j = tid; j < a.k; j += kWG) a.eob[j] = L.ids[j];
     return;
   }
   // metadata of experts [e_lo, e_lo + EL), numbered from 0
@@ -1930,6 +1972,26 @@ KernelFn pick_fixed_group(bool small, int seg, int epl, bool bf16, int mode, int
   return nullptr;
 }
 
+// Precomputed keys (LOAD_KEYS), 64-lane segments: the usual experts per lane
+// compiled as constants, BF16 rows of 896 experts in 8 groups also with the
+// lanes per group (8) fixed; other layouts read both at run time.
+template <bool BF16>
+KernelFn pick1_keys_small(int epl) {
+  switch (epl) {
+    case 1: return k_small<64, 1, BF16, LOAD_KEYS>;
+    case 2: return k_small<64, 2, BF16, LOAD_KEYS>;
+    case 4: return k_small<64, 4, BF16, LOAD_KEYS>;
+    case 8: return k_small<64, 8, BF16, LOAD_KEYS>;
+    case 14: return k_small<64, 14, BF16, LOAD_KEYS>;
+    case 16: return k_small<64, 16, BF16, LOAD_KEYS>;
+    default: return k_small<64, 0, BF16, LOAD_KEYS>;
+  }
+}
+KernelFn pick_keys_small(int epl, bool bf16, int lpg) {
+  if (bf16 && epl == 14 && lpg == 8) return k_small<64, 14, true, LOAD_KEYS, 8>;
+  return bf16 ? pick1_keys_small<true>(epl) : pick1_keys_small<false>(epl);
+}
+
 // Optional HIP events of one call (diagnostics): launch i is made with
 // hipExtLaunchKernel, which stamps ev[2i] and ev[2i+1] with the start and end
 // of that kernel's own execution.
@@ -2183,10 +2245,19 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.stage_bytes = 0;
     a.nbuf = 1;
   }
-  a.tbl = (a.fast && bf16) ? 1 : 0;
+  // Small batches (one token per wave, at most kKeysPreMax keys): the
+  // workgroup computes every exact key into LDS up front, about one per
+  // thread, instead of copying the 32 KiB table and reading rows per wave.
+  a.keys_pre = 0;
+  if (want_small && a.fast && a.seg == kWave && M <= kNW && (int64_t)M * E <= kKeysPreMax) {
+    a.keys_pre = 1;
+    a.stage_bytes = 8 * E;  // E keys then E scores per token
+    a.nbuf = 1;
+  }
+  a.tbl = (a.fast && bf16 && !a.keys_pre) ? 1 : 0;
   a.bias_dma = (aligned(bias, 16) && E % 4 == 0) ? 1 : 0;
-  const int mode = a.stage_bytes ? LOAD_STAGE : LOAD_VEC;
-  const size_t stg = stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes);
+  const int mode = a.keys_pre ? LOAD_KEYS : (a.stage_bytes ? LOAD_STAGE : LOAD_VEC);
+  const size_t stg = stage_total(a.fast, a.seg, a.nbuf, a.stage_bytes, a.keys_pre ? M : 0);
 
   const bool small_fits =
       M <= kTwMax && lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, M, k, a.tbl).total <= kLdsLimit;
@@ -2202,7 +2273,9 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.rows_first = 1;
     const size_t lds = lds_plan(KIND_SMALL, E, n_group, a.gstage, stg, a.tw, k, a.tbl).total;
     void* params[] = {&a};
-    KernelFn kf = a.gstage ? pick_fixed_group(true, a.seg, a.epl, bf16, mode, a.seg / n_group) : nullptr;
+    KernelFn kf = nullptr;
+    if (a.keys_pre) kf = pick_keys_small(a.epl, bf16, a.gstage ? a.seg / n_group : 0);
+    else if (a.gstage) kf = pick_fixed_group(true, a.seg, a.epl, bf16, mode, a.seg / n_group);
     if (!kf) kf = pick_k_small(a.seg, a.epl, bf16, mode);
     const void* fn = reinterpret_cast<const void*>(kf);
     if (a.tbl && !no_static_lds(fn)) return MRS_ERR_LAUNCH;
