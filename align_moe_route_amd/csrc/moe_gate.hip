@@ -46,22 +46,80 @@ __device__ __forceinline__ void unpack8(const uint4 q, double* f) {
 }
 
 // One workgroup per expert: its 256 threads split the weight row (thread i
-// takes vectors i, i + 256, ...), so a row's loads are all in flight at once;
-// the partial sums meet in LDS.
+// takes vectors i, i + 256, ..., at most NJ of them).  Every weight vector of
+// the thread, and the hidden vectors of the first TOK tokens, are requested
+// before the first one is used, so a row's bytes are in flight together
+// rather than one round trip per vector; the weight vectors stay in
+// registers for the later tokens.  The partial sums meet in LDS.  Each
+// thread accumulates its vectors in index order, as a plain loop would.
+template <int NJ, int TOK>
 __global__ __launch_bounds__(kGateWaves * 64) void k_gate(const uint16_t* __restrict__ hidden,
                                                           const uint16_t* __restrict__ w, float* logits, int M,
                                                           int E, int H) {
   constexpr int kT = kGateWaves * 64;
-  __shared__ double part[kGateTok][kGateWaves];
+  __shared__ double part[TOK][kGateWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = blockIdx.x;
   const int nv = H / 8;  // 16-byte vectors per row
+  const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)e * H);
+  uint4 wq[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) wq[j] = wr[min(tid + j * kT, nv - 1)];  // clamped: inside the row
+  for (int t0 = 0; t0 < M; t0 += TOK) {
+    uint4 hq[TOK][NJ];
+#pragma unroll
+    for (int q = 0; q < TOK; ++q) {
+      const uint4* hr = reinterpret_cast<const uint4*>(hidden + (size_t)min(t0 + q, M - 1) * H);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) hq[q][j] = hr[min(tid + j * kT, nv - 1)];
+    }
+    double acc[TOK];
+#pragma unroll
+    for (int q = 0; q < TOK; ++q) acc[q] = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (tid + j * kT < nv) {
+        double wf[8];
+        unpack8(wq[j], wf);
+#pragma unroll
+        for (int q = 0; q < TOK; ++q) {
+          double hf[8];
+          unpack8(hq[q][j], hf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[q] = fma(hf[i], wf[i], acc[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TOK; ++q) {
+      const double s = wave_sum(acc[q]);
+      if (lane == 0) part[q][wv] = s;
+    }
+    __syncthreads();
+    if (tid < TOK && t0 + tid < M) {
+      double s = 0.0;
+#pragma unroll
+      for (int q = 0; q < kGateWaves; ++q) s += part[tid][q];
+      logits[(size_t)(t0 + tid) * E + e] = (float)s;
+    }
+    __syncthreads();  // part is reused by the next pass
+  }
+}
+
+// Longer rows (more than 8 vectors per thread): one vector at a time.
+__global__ __launch_bounds__(kGateWaves * 64) void k_gate_long(const uint16_t* __restrict__ hidden,
+                                                               const uint16_t* __restrict__ w, float* logits,
+                                                               int M, int E, int H) {
+  constexpr int kT = kGateWaves * 64;
+  __shared__ double part[kGateTok][kGateWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x;
+  const int nv = H / 8;
   const uint4* wr = reinterpret_cast<const uint4*>(w + (size_t)e * H);
   for (int t0 = 0; t0 < M; t0 += kGateTok) {
     double acc[kGateTok];
 #pragma unroll
     for (int j = 0; j < kGateTok; ++j) acc[j] = 0.0;
-#pragma unroll 4
     for (int c = tid; c < nv; c += kT) {
       double wf[8];
       unpack8(wr[c], wf);
@@ -87,10 +145,26 @@ __global__ __launch_bounds__(kGateWaves * 64) void k_gate(const uint16_t* __rest
       for (int q = 0; q < kGateWaves; ++q) s += part[tid][q];
       logits[(size_t)(t0 + tid) * E + e] = (float)s;
     }
-    __syncthreads();  // part is reused by the next pass
+    __syncthreads();
   }
 }
 
+template <int TOK>
+const void* gate_kernel_tok(int nj) {
+  switch (nj) {
+    case 1: return reinterpret_cast<const void*>(k_gate<1, TOK>);
+    case 2: return reinterpret_cast<const void*>(k_gate<2, TOK>);
+    case 3:
+    case 4: return reinterpret_cast<const void*>(k_gate<4, TOK>);
+    default: return reinterpret_cast<const void*>(k_gate<8, TOK>);
+  }
+}
+// vectors per thread rounded up to 1, 2, 4 or 8; one token per pass at M = 1
+const void* gate_kernel(int M, int H) {
+  const int nj = (H / 8 + kGateWaves * 64 - 1) / (kGateWaves * 64);
+  if (nj > 8) return reinterpret_cast<const void*>(k_gate_long);
+  return M == 1 ? gate_kernel_tok<1>(nj) : gate_kernel_tok<kGateTok>(nj);
+}
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -112,8 +186,7 @@ extern "C" int moe_gate_route_sort(const void* hidden, const void* w_gate, const
     const uint16_t* w16 = static_cast<const uint16_t*>(w_gate);
     void* params[] = {&h16, &w16, &out_logits, &M, &E, &H};
     const dim3 grid((unsigned)E);
-    if (hipLaunchKernel(reinterpret_cast<const void*>(k_gate), grid, dim3(kGateWaves * 64), params, 0, st) !=
-        hipSuccess)
+    if (hipLaunchKernel(gate_kernel(M, H), grid, dim3(kGateWaves * 64), params, 0, st) != hipSuccess)
       return MRS_ERR_LAUNCH;
   }
   // M <= 64: the route-sort runs in one workgroup (asked for explicitly), so it
