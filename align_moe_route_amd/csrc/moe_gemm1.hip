@@ -12,10 +12,11 @@
 // tiles into registers while the waves run v_mfma_f32_32x32x16_bf16 on the
 // current LDS tiles, then stores them into the other LDS buffer (one barrier
 // per step).  LDS rows are XOR-swizzled by
-// 16-byte chunk (swz below).  The column tiles of one row tile run back to
-// back on one XCD (tile_of below), so its gathered rows of x are fetched into
-// that XCD's L2 once.  num_post_pad is read on the device: tiles past it
-// exit.
+// 16-byte chunk (swz below).  Each XCD takes runs of 8 consecutive row tiles
+// (mostly one expert's) and, within a run, the row tiles of one column tile
+// one after another (tile_of below), so the workgroups running together on
+// an XCD share that expert's weight column tile in its L2.  num_post_pad is
+// read on the device: tiles past it exit.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -54,15 +55,22 @@ struct GArgs {
 // of bank conflicts whether the LDS serves 128 or 256 bytes per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 7) ^ ((r >> 3) & 1)); }
 
-// MI355X dispatches workgroup h to XCD h mod 8.  Workgroups h = 8 (ntn G + j)
-// + x, j < ntn, all run on XCD x and take row tile 8 G + x with column tile
-// j: the ntn column tiles of a row tile are dispatched one after another on
-// the same XCD.  Returns false for the padding workgroups of the last group.
+// MI355X dispatches workgroup h to XCD h mod 8.  XCD x's j-th workgroup
+// (h = 8 j + x) takes, in run m = j / (R ntn), column tile (j / R) mod ntn of
+// row tile (8 m + x) R + j mod R: runs of R = kRunRows consecutive row tiles
+// go to the XCDs in turn, and inside a run the R row tiles of a column tile
+// are dispatched together.  On the 8192 x 896 prefill metadata this cut the
+// bytes fetched past the L2 from 5.8 to 4.1 GB per call (row tiles dealt
+// one by one to the XCDs: every XCD fetched every expert's weights) and the
+// time by 2-3 %.  The grid covers whole runs; workgroups past the last row
+// tile return false.
 constexpr int kXcds = 8;
+constexpr int kRunRows = 8;
 __device__ __forceinline__ bool tile_of(int h, int ntn, int nrt, int& rt, int& ct) {
-  const int x = h % kXcds, j = (h / kXcds) % ntn, G = h / (kXcds * ntn);
-  rt = G * kXcds + x;
-  ct = j;
+  const int x = h % kXcds, j = h / kXcds;
+  const int m = j / (kRunRows * ntn), c = (j / kRunRows) % ntn, r = j % kRunRows;
+  rt = (m * kXcds + x) * kRunRows + r;
+  ct = c;
   return rt < nrt;
 }
 
@@ -210,7 +218,8 @@ int gemm1_impl(const void* x, const void* w, const int32_t* sorted_ids, const in
   const int bm = block % 128 == 0 ? 128 : (block % 64 == 0 ? 64 : 32);
   const int bn = (bm >= 64 && N % 256 == 0) ? 256 : 128;
   const int64_t nrt = row_limit / bm, ntn = N / bn;
-  const int64_t groups = (nrt + kXcds - 1) / kXcds;
+  // whole runs of kRunRows row tiles on every XCD (tile_of)
+  const int64_t groups = ((nrt + kXcds * kRunRows - 1) / (kXcds * kRunRows)) * kRunRows;
   if (groups * kXcds * ntn > INT32_MAX) return MRS_ERR_OVERFLOW;
   GArgs g{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), sorted_ids, expert_of_block,
           num_post_pad, static_cast<uint16_t*>(y), M, k, E, K, N, block, (int)row_limit, (int)nrt};
