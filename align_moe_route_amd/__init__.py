@@ -207,7 +207,8 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             (calls on different streams may then overlap in time).  Make the
             first call on a stream before capturing a graph on it, or the
             allocation and zero fill of that buffer join the graph.
-    stats:  optional int32 [2] device tensor (exact-path / fast-path token counts).
+    stats:  optional int32 [3] device tensor (tokens decided by the workgroup-wide
+            exact selection / by one wave / redone with exact keys by one wave).
     events: optional list of 6 torch.cuda.Event(enable_timing=True); events
             2i and 2i+1 take the start and end of the call's kernel i (pairs
             past the last kernel are recorded after it); returns
@@ -255,7 +256,7 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
     else:
         _check_route_output(out, M, k, rows, blocks, dev)
     if stats is not None:
-        _check_tensor(stats, dev, torch.int32, 2, "stats")
+        _check_tensor(stats, dev, torch.int32, 3, "stats")
     nbytes = workspace_bytes(M, E, k, block)
     if stream is None:
         stream = torch.cuda.current_stream(dev)

@@ -1177,7 +1177,10 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     L.bits[e] = 0ull;
     if (!a.bias_dma) L.bias[e] = a.bias[e];
   }
-  if (tid == 0) L.misc[0] = 0;
+  if (tid == 0) {
+    L.misc[0] = 0;  // tokens for the workgroup-wide exact selection
+    L.misc[3] = 0;  // tokens redone with exact keys by their wave (statistics)
+  }
   if constexpr (MODE == LOAD_KEYS) {
     // every exact key and score of the batch, one (token, expert) per thread
     // and pass: RN32 sigmoid (float64 quotient, double-double when it lies
@@ -1272,6 +1275,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
         st = st == TOK_REDO_EXACT ? TOK_DONE : st;
       } else if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
         const bool redo = act && st == TOK_REDO_EXACT;
+        if (a.stats && redo && ls == 0) atomicAdd(&L.misc[3], 1);
         const int st2 =
             lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true, av, false, tn);
         if (redo) st = st2;
@@ -1285,6 +1289,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
       const int it = __builtin_ctzll(redo_rounds);
       redo_rounds &= redo_rounds - 1;
       const int tl = tok_of(it);
+      if (a.stats && ls == 0) atomicAdd(&L.misc[3], 1);
       const int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, true, t0 + tl, tl, stg, bv, delta, epsg, true, av,
                                                            false, -1);
       if (st == TOK_ESCALATE && ls == 0) {
@@ -1305,6 +1310,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], nesc);
     atomicAdd(&a.stats[1], nt - nesc);
+    atomicAdd(&a.stats[2], L.misc[3]);
   }
   __syncthreads();
 }

@@ -80,11 +80,11 @@ def assert_parity(inp, g, tokens=None):
 def test_workload_parity(name):
     cfg = workloads.CONFIGS[name]
     inp = workloads.make_inputs(cfg)
-    stats = torch.zeros(2, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(3, dtype=torch.int32, device="cuda")
     g = run(inp, stats=stats)
     st = stats.cpu().numpy()
-    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}", flush=True)
-    assert st.sum() == cfg.M
+    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, redone in the wave {st[2]}", flush=True)
+    assert st[0] + st[1] == cfg.M
     assert_parity(inp, g)
 
 
@@ -153,6 +153,15 @@ SWEEP = [
     (90, 4096, 16, 8, 3, 64, "f32", "hot"),           # 8-lane groups, 16-lane blocks
     (75, 4096, 16, 16, 8, 128, "f32", "coarse"),      # 4-lane groups, 8-lane blocks, many exact ties
     (80, 4096, 8, 32, 10, 32, "f32", "shared"),       # 2-lane groups, 4-lane blocks
+    # FP32 rows in the key registers with the next row requested early, two
+    # tokens per wave: runs of 20 and 40 experts (run-time length), and pairs
+    # of equal keys (group boundaries redone with exact keys after the loop)
+    (5000, 1280, 16, 4, 2, 64, "f32", "normal"),
+    (5000, 2560, 16, 8, 4, 64, "f32", "duplicated"),
+    # small batches with the keys computed by the whole workgroup up front
+    (2, 896, 16, 8, 4, 32, "bf16", "shared"),         # 14 experts per lane, 8 lanes per group fixed
+    (16, 128, 8, 4, 2, 16, "f32", "equal"),           # one token per wave, all keys equal
+    (1, 2048, 16, 8, 4, 32, "f32", "normal"),         # 32 experts per lane (run-time length)
     # at the limits of the contract: k = 64 with E = 4096, thousands of groups,
     # groups of one expert, blocks larger than any expert's count
     (40, 4096, 64, 1, 1, 1024, "bf16", "normal"),      # one group, 1024-row blocks
@@ -366,7 +375,7 @@ def test_binding_refuses_host_buffers():
                        workspace=torch.zeros(1 << 16, dtype=torch.uint8))
     with pytest.raises(ValueError):
         amr.route_sort(x, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block,
-                       stats=torch.zeros(2, dtype=torch.int32))
+                       stats=torch.zeros(3, dtype=torch.int32))
     srt = amr.sort_from_ids(good.ids, cfg.E, cfg.block)
     torch.cuda.synchronize()
     for field in srt._fields:
@@ -455,11 +464,37 @@ def test_concurrent_streams_default_workspace():
 def test_stats_count_every_token():
     cfg = workloads.CONFIGS["threshold"]
     inp = workloads.make_inputs(cfg)
-    stats = torch.zeros(2, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(3, dtype=torch.int32, device="cuda")
     run(inp, stats=stats)
     run(inp, flags=amr.FLAG_FORCE_EXACT, stats=stats)
     st = stats.cpu().numpy()
-    assert st.sum() == 2 * cfg.M and st[0] >= cfg.M
+    assert st[0] + st[1] == 2 * cfg.M and st[0] >= cfg.M and st[2] == 0  # BF16: never redone
+
+
+@pytest.mark.parametrize("case", [
+    # FP32 rows in the key registers, two tokens per wave: redone after the loop
+    (5000, 2560, 16, 8, 4, 64, "f32", "duplicated"),
+    # 32-lane segments (two tokens per wave): redone in place
+    (5000, 896, 16, 8, 4, 128, "f32", "equal"),
+    # one token per wave, rows staged in LDS (14 experts per lane): redone in place
+    (200, 896, 16, 8, 4, 32, "f32", "equal"),
+], ids=lambda c: "M{}_E{}".format(c[0], c[1]))
+def test_exact_redo_in_the_wave(case):
+    """Equal group scores (pairs of identical keys; all keys equal) leave the
+    group boundary of the fast keys uncertain, so the wave redoes those
+    tokens with exact keys: the redo paths are taken, and every token still
+    matches the oracle (with all keys equal the exact pass then hands the
+    token to the workgroup-wide selection)."""
+    M, E, k, ng, tg, block, dtype, dist = case
+    print(f"[gpu] exact redo M={M} E={E} {dtype} {dist}", flush=True)
+    inp = workloads.make_inputs(workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=3))
+    stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+    g = run(inp, stats=stats)
+    st = stats.cpu().numpy()
+    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, redone in the wave {st[2]}", flush=True)
+    assert st[0] + st[1] == M
+    assert st[2] > 0
+    assert_parity(inp, g)
 
 
 # ---------------------------------------------------------------------------
