@@ -9,7 +9,12 @@
 // Workgroups of 1024 threads (16 waves) take tw = ceil(M / 256) consecutive
 // tokens each (one workgroup per compute unit at the 8192-token shape); the
 // rows are copied into LDS with global_load_lds (wave by wave, so a wave's
-// compute overlaps the others' copies) or read as 16-byte vectors.
+// compute overlaps the others' copies) or read as 16-byte vectors.  Long FP32
+// rows read as vectors go straight into the key registers, and a wave
+// requests the first half of its next token's row as soon as the current
+// token's keys are no longer needed (see lean_token).  Small batches (one
+// token per wave, at most kKeysPreMax keys) have the whole workgroup compute
+// every exact key into LDS first (LOAD_KEYS).
 //
 // Selection, one token per wave segment of 32 or 64 lanes; lane l owns
 // experts [l*epl, (l+1)*epl), or, for FP32 rows read as 16-byte vectors with
@@ -22,7 +27,8 @@
 //      group score, rank of every group by (score desc, index asc) by counting
 //      in LDS.  With fast keys the kept set is accepted only if it beats the
 //      dropped groups by more than the fast scores' error, else the token is
-//      redone in the same wave with correctly rounded keys;
+//      redone by its wave with correctly rounded keys (in place, or after the
+//      wave's last token when the row lives in the key registers);
 //   3. threshold: a lower bound of the k-th largest of the kept lanes' top-two
 //      keys (at least k keys reach it), by ballot-count bisection over the
 //      highest differing bits; with fast keys it is lowered by 2*delta;
@@ -43,7 +49,8 @@
 //   between workgroups inside one launch needs agent-scope (cross-XCD) memory
 //   round trips of about 2 us each on MI355X; the two kernel boundaries cost
 //   less than the two device-wide waits that would replace them.
-// M <= 64: everything in one workgroup and one launch.
+// M <= 64 (while faster): everything in one workgroup and one launch; at
+//   most 192 tokens: two launches (the scatter folds the column scan in).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
