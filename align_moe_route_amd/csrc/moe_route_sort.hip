@@ -1133,6 +1133,20 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 // Selection of tokens [t0, t0+nt) by one workgroup, with the histogram bitsets
 // and the per-token expert lists in LDS.  Wave w, round it takes tokens
 // (it*kNW + w)*NSEG + segment.
+// One token over all experts: its k picks are distinct and ascending, so pick
+// j owns rows [j*block, (j+1)*block) -- its slot j, then sentinels (M*k = k)
+// -- and block j; no scan over the experts is needed, and only the blocks'
+// experts (expert_of_block) depend on the selection.  Threads i0, i0+stride,
+// ... write the rows and num_post_pad.
+__device__ void one_token_rows(const Args& a, int i0, int stride) {
+  const int rows = a.k * a.block;
+  for (int r = i0; r < rows; r += stride) {
+    const int j = div_block(r, a);
+    a.sorted_ids[r] = r == j * a.block ? j : a.k;
+  }
+  if (i0 == 0) *a.npp = rows;
+}
+
 template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   constexpr int NSEG = kWave / SEG;
@@ -1160,7 +1174,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
                                        (__attribute__((address_space(3))) void*)(size_t)(j * kWG * 16 + wbase), 16,
                                        0, 0);
   }
-  if (a.bias_dma) {
+  if (MODE != LOAD_KEYS && a.bias_dma) {  // precomputed keys already hold the bias
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.bias);
     unsigned char* dst = reinterpret_cast<unsigned char*>(L.bias);
     const int chunks = a.E / 4;
@@ -1182,7 +1196,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   }
   for (int e = tid; e < a.E; e += kWG) {
     L.bits[e] = 0ull;
-    if (!a.bias_dma) L.bias[e] = a.bias[e];
+    if (MODE != LOAD_KEYS && !a.bias_dma) L.bias[e] = a.bias[e];
   }
   if (tid == 0) {
     L.misc[0] = 0;  // tokens for the workgroup-wide exact selection
@@ -1207,7 +1221,7 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
       }
     }
   }
-  if (a.tbl || a.bias_dma) {
+  if (MODE != LOAD_KEYS && (a.tbl || a.bias_dma)) {
     // loads complete in order: with R row copies issued after the shared
     // data, vmcnt <= R means the table and bias copies of this wave are done
     constexpr int R = EPL > 0 ? row_dma_count<SEG, EPL, BF16 ? 2 : 4>() : 0;
@@ -1215,6 +1229,12 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     else wait_vmem_all();
   }
   __syncthreads();
+  if constexpr (MODE == LOAD_KEYS) {
+    // one token over all experts: the waves without a token write the sorted
+    // rows, which do not depend on the selection, while wave 0 selects (and
+    // their store counts never reach wave 0's waits)
+    if (a.M == 1 && a.e_lo == 0 && a.EL == a.E && w > 0) one_token_rows(a, tid - kWave, kWG - kWave);
+  }
   if (late && a.fast && MODE == LOAD_STAGE) {
     const int tl = tok_of(0);
     stage_rows_async<SEG, EPL>(a, stg, sb, tl < 0 ? -1 : t0 + tl, BF16 ? 2 : 4);
@@ -1402,20 +1422,10 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   const Lds L = carve(KIND_SMALL, a);
   const int tid = threadIdx.x;
   const bool one = a.M == 1 && a.e_lo == 0 && a.EL == a.E;
-  if (one) {
-    // one token over all experts: its k picks are distinct and ascending, so
-    // pick j owns rows [j*block, (j+1)*block) -- its slot j, then sentinels
-    // (M*k = k) -- and block j; no scan over the experts is needed, and only
-    // the block's expert depends on the selection
-    const int rows = a.k * a.block;
-    for (int r = tid; r < rows; r += kWG) {
-      const int j = div_block(r, a);
-      a.sorted_ids[r] = r == j * a.block ? j : a.k;
-    }
-    if (tid == 0) *a.npp = rows;
-  }
   select_tokens<SEG, EPL, BF16, MODE, LPG>(a, L, 0, a.M);
   if (one) {
+    // (precomputed keys: the rows were written during the selection)
+    if constexpr (MODE != LOAD_KEYS) one_token_rows(a, tid, kWG);
     for (int j = tid; j < a.k; j += kWG) a.eob[j] = L.ids[j];
     return;
   }
