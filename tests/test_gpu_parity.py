@@ -394,8 +394,16 @@ def test_determinism_across_runs_and_paths():
         assert np.array_equal(g["w"].view(np.uint32), base["w"].view(np.uint32)) or flags
 
 
-def test_graph_replay_with_changed_inputs():
-    cfg = workloads.custom(512, 896, 16, 8, 4, 64, "bf16", "normal", seed=30)
+@pytest.mark.parametrize("shape", [
+    (512, 896, 16, 8, 4, 64, "bf16"),    # three launches
+    (1, 896, 16, 8, 4, 32, "bf16"),      # one token: keys precomputed, rows written by the idle waves
+    (4, 64, 4, 8, 4, 16, "f32"),         # keys precomputed, FP32
+    (5000, 2560, 16, 8, 4, 64, "f32"),   # FP32 rows in the key registers, next rows requested early
+], ids=lambda c: "M{}_E{}_{}".format(c[0], c[1], c[6]))
+def test_graph_replay_with_changed_inputs(shape):
+    M, E, k, ng, tg, block, dtype = shape
+    print(f"[gpu] graph replay M={M} E={E} {dtype}", flush=True)
+    cfg = workloads.custom(M, E, k, ng, tg, block, dtype, "normal", seed=30)
     sets = [workloads.make_inputs(cfg, seed=s) for s in range(4)]
     x, b = to_gpu(sets[0])
     stream = torch.cuda.Stream()
