@@ -1206,18 +1206,36 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     // every exact key and score of the batch, one (token, expert) per thread
     // and pass: RN32 sigmoid (float64 quotient, double-double when it lies
     // near a rounding midpoint) plus the bias
+    // Pair i = tl * E + e goes to thread i mod kWG, so the pairs of a batch
+    // spread over every wave; both of a thread's logits are requested before
+    // the first sigmoid.
+    static_assert(kKeysPreMax <= 2 * kWG, "at most two (token, expert) pairs per thread");
     const int row_f = a.stage_bytes / 4;  // floats per token: E keys, then E scores
     float* kf = reinterpret_cast<float*>(L.stage);
-    for (int e = tid; e < a.E; e += kWG) {
-      const float b = a.bias[e];  // requested together with the first logit
-      for (int tl = 0; tl < nt; ++tl) {
-        const float x = load_logit<BF16>(a.logits, (size_t)(t0 + tl) * a.E + e);
+    const int np = nt * a.E;
+    const int npass = np > kWG ? 2 : 1;  // wave-uniform
+    float xv[2], bv2[2];
+    int tlv[2], ev[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < npass) {
+        const int i = tid + j * kWG;
+        const int ii = i < np ? i : 0;  // past the last pair: a valid dummy read
+        tlv[j] = ii / a.E;
+        ev[j] = ii - tlv[j] * a.E;
+        bv2[j] = a.bias[ev[j]];
+        xv[j] = load_logit<BF16>(a.logits, (size_t)(t0 + tlv[j]) * a.E + ev[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < npass && tid + j * kWG < np) {
         bool amb;
         float up;
-        float sc = sigrn::sigmoid_rn32_try(x, amb, up);
-        if (amb) sc = sigmoid_settle(x, sc, up);
-        kf[tl * row_f + e] = sc + b;
-        kf[tl * row_f + a.E + e] = sc;
+        float sc = sigrn::sigmoid_rn32_try(xv[j], amb, up);
+        if (amb) sc = sigmoid_settle(xv[j], sc, up);
+        kf[tlv[j] * row_f + ev[j]] = sc + bv2[j];
+        kf[tlv[j] * row_f + a.E + ev[j]] = sc;
       }
     }
   }
@@ -2011,7 +2029,10 @@ KernelFn pick1_keys_small(int epl) {
   }
 }
 KernelFn pick_keys_small(int epl, bool bf16, int lpg) {
-  if (bf16 && epl == 14 && lpg == 8) return k_small<64, 14, true, LOAD_KEYS, 8>;
+  // eight lanes per group: the 896-expert shape (BF16 decode, FP32 gate
+  // output) and 64 experts in 8 groups
+  if (epl == 14 && lpg == 8) return bf16 ? k_small<64, 14, true, LOAD_KEYS, 8> : k_small<64, 14, false, LOAD_KEYS, 8>;
+  if (epl == 1 && lpg == 8) return bf16 ? k_small<64, 1, true, LOAD_KEYS, 8> : k_small<64, 1, false, LOAD_KEYS, 8>;
   return bf16 ? pick1_keys_small<true>(epl) : pick1_keys_small<false>(epl);
 }
 
