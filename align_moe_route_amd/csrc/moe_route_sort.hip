@@ -1357,7 +1357,8 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     atomicAdd(&a.stats[1], nt - nesc);
     atomicAdd(&a.stats[2], L.misc[3]);
   }
-  __syncthreads();
+  // no barrier here: the bitsets and expert lists were complete at the one
+  // above, and exact_token_wg ends with its own
 }
 
 // Exclusive scan of padded counts over all experts into L.off; returns the
@@ -1449,9 +1450,27 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   }
   // metadata of experts [e_lo, e_lo + EL), numbered from 0
   const unsigned long long* bits = L.bits + a.e_lo;
+  const int sentinel = a.M * a.k;
+  if (a.EL <= kWave && sentinel <= 4 * kWave) {
+    // one expert per lane and a few routes: wave 0 writes all of the metadata
+    // (offsets by a wave scan, no workgroup barrier)
+    if (tid >= kWave) return;
+    const int c = tid < a.EL ? __popcll(bits[tid]) : 0;
+    const int p = pad_block(c, a);
+    const int incl = wave_incl_scan(p);
+    if (tid < a.EL) L.off[tid] = incl - p;
+    if (tid == 0) *a.npp = (int)readlane((uint32_t)incl, kWave - 1);
+    wave_sync_lds();
+    write_padding(a, a.EL, L.off, [&](int e) { return __popcll(bits[e]); });
+    for (int q = tid; q < sentinel; q += kWave) {
+      const int e = L.ids[q] - a.e_lo;
+      if ((unsigned)e < (unsigned)a.EL)
+        a.sorted_ids[L.off[e] + __popcll(bits[e] & ((1ull << (q / a.k)) - 1ull))] = q;
+    }
+    return;
+  }
   const int total = expert_offsets(a, L, a.EL, [&](int e) { return pad_block(__popcll(bits[e]), a); });
   if (tid == 0) *a.npp = total;
-  const int sentinel = a.M * a.k;
   write_padding(a, a.EL, L.off, [&](int e) { return __popcll(bits[e]); });
   for (int q = tid; q < sentinel; q += kWG) {
     const int tl = q / a.k;
