@@ -407,6 +407,9 @@ __device__ __forceinline__ float butterfly_partner(float v, int lev) {
 // ----------------------------------------------------------------------------
 // Workgroup-level helpers (all kWG threads must call them).
 // ----------------------------------------------------------------------------
+// REUSE = false: the caller writes L.scan no more before its next barrier, so
+// the barrier that protects the wave totals from a later scan is left out.
+template <bool REUSE = true>
 __device__ int wg_excl_scan(const Lds& L, int v) {
   const int w = threadIdx.x >> 6;
   const int x = wave_incl_scan(v);
@@ -414,7 +417,7 @@ __device__ int wg_excl_scan(const Lds& L, int v) {
   __syncthreads();
   int pre = 0;
   for (int q = 0; q < w; ++q) pre += L.scan[q];
-  __syncthreads();
+  if (REUSE) __syncthreads();
   return pre + x - v;
 }
 
@@ -1377,7 +1380,7 @@ __device__ int expert_offsets(const Args& a, const Lds& L, int n, F padded) {
       local += p;
     }
   }
-  int pre = wg_excl_scan(L, local);
+  int pre = wg_excl_scan<false>(L, local);
   for (int i = 0; i < ept; ++i) {
     const int e = e0 + i;
     if (e < n) {
@@ -1671,7 +1674,7 @@ __global__ __launch_bounds__(kWG) void k_scatter(Args a) {
   int local = 0;
 #pragma unroll
   for (int i = 0; i < kEPerThread; ++i) local += pv[i];
-  int pre = wg_excl_scan(L, local);
+  int pre = wg_excl_scan<false>(L, local);
 #pragma unroll
   for (int i = 0; i < kEPerThread; ++i) {
     const int e = tid * ept + i;
