@@ -162,6 +162,11 @@ SWEEP = [
     (2, 896, 16, 8, 4, 32, "bf16", "shared"),         # 14 experts per lane, 8 lanes per group fixed
     (16, 128, 8, 4, 2, 16, "f32", "equal"),           # one token per wave, all keys equal
     (1, 2048, 16, 8, 4, 32, "f32", "normal"),         # 32 experts per lane (run-time length)
+    # one workgroup, at most 64 experts: wave 0 writes the metadata up to 256
+    # routes, the workgroup scan beyond
+    (32, 64, 8, 8, 4, 16, "f32", "normal"),           # 256 routes
+    (33, 64, 8, 8, 4, 16, "bf16", "hot"),             # 264 routes
+    (56, 64, 4, 2, 1, 4, "f32", "duplicated"),        # 224 routes, four-row blocks
     # at the limits of the contract: k = 64 with E = 4096, thousands of groups,
     # groups of one expert, blocks larger than any expert's count
     (40, 4096, 64, 1, 1, 1024, "bf16", "normal"),      # one group, 1024-row blocks
