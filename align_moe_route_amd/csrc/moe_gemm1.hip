@@ -8,7 +8,7 @@
 // BM divides the padding block, so the tile's rows all belong to one expert:
 // expert_of_block gives the weight matrix, sorted_ids gives the token of each
 // row (a padding row stores zeros into LDS and so produces zeros).  The K loop
-// steps by 64: every thread fetches its 16-byte chunks of the next x and W
+// steps by 32 or 64 (k_gemm1): every thread fetches its 16-byte chunks of the next x and W
 // tiles into registers while the waves run v_mfma_f32_32x32x16_bf16 on the
 // current LDS tiles, then stores them into the other LDS buffer (one barrier
 // per step).  LDS rows are XOR-swizzled by
@@ -31,8 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 64;                   // K per pipeline step
-constexpr int kChunks = kBK / 8;          // 16-byte chunks per tile row
+constexpr int kKAlign = 64;  // K is a multiple of this (every tile's K step divides it)
 
 struct GArgs {
   const uint16_t* x;
@@ -53,7 +52,17 @@ struct GArgs {
 // any sixteen starting at a multiple of 16 from sixteen distinct positions of
 // a 256-byte line, so the MFMA operand reads (32 rows at one chunk) are free
 // of bank conflicts whether the LDS serves 128 or 256 bytes per cycle.
-__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 7) ^ ((r >> 3) & 1)); }
+//
+// With 64-byte rows (K steps of 32: four chunks) two rows share a 128-byte
+// line, and the chunk index is XORed with ((r >> 1) ^ (r >> 3)) mod 4: any
+// eight rows starting at a multiple of 8 again land on eight distinct 16-byte
+// positions of a 128-byte line, and any sixteen starting at a multiple of 16
+// on sixteen of a 256-byte line.
+template <int CH>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CH == 8) return r * CH + (c ^ (r & 7) ^ ((r >> 3) & 1));
+  else return r * CH + (c ^ (((r >> 1) ^ (r >> 3)) & 3));
+}
 
 // MI355X dispatches workgroup h to XCD h mod 8.  XCD x's j-th workgroup
 // (h = 8 j + x) takes, in run m = j / (R ntn), column tile (j / R) mod ntn of
@@ -82,10 +91,17 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 // A BM x BN tile per workgroup of BN / 32 waves (each wave 64 x 64 when
-// BM >= 64): the 256-column tile halves the x traffic per MFMA.
+// BM >= 64): the 256-column tile halves the x traffic per MFMA.  The K step
+// is 32 when every thread still has an x chunk to fetch (BM * 4 >= threads):
+// the two LDS buffers then take 48 KiB for the 128 x 256 tile, so two
+// workgroups share a compute unit (on the 8192 x 896 prefill metadata, 3-4 %
+// faster than K steps of 64 with one workgroup per compute unit).
 template <int BM, int BN>
 __global__ __launch_bounds__(BN * 2) void k_gemm1(GArgs g) {
   constexpr int kThreads = BN * 2;
+  constexpr int kBK = BM * 4 >= kThreads ? 32 : 64;  // K per pipeline step
+  constexpr int kChunks = kBK / 8;                    // 16-byte chunks per tile row
+  static_assert(kKAlign % kBK == 0, "K step");
   constexpr int NW = kThreads / 64;
   constexpr int WGM = BM >= 64 ? 2 : 1;   // waves along the rows
   constexpr int WGN = NW / WGM;           // waves along the columns
@@ -142,12 +158,12 @@ __global__ __launch_bounds__(BN * 2) void k_gemm1(GArgs g) {
 #pragma unroll
     for (int p = 0; p < AP; ++p) {
       const int idx = tid + p * kThreads;
-      As[buf][swz(idx / kChunks, idx % kChunks)] = av[p] ? ra[p] : u32x4{0u, 0u, 0u, 0u};
+      As[buf][swz<kChunks>(idx / kChunks, idx % kChunks)] = av[p] ? ra[p] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int p = 0; p < BP; ++p) {
       const int idx = tid + p * kThreads;
-      Bs[buf][swz(idx / kChunks, idx % kChunks)] = rb[p];
+      Bs[buf][swz<kChunks>(idx / kChunks, idx % kChunks)] = rb[p];
     }
   };
 
@@ -173,10 +189,10 @@ __global__ __launch_bounds__(BN * 2) void k_gemm1(GArgs g) {
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, As[cur][swz(wm * WTM + i * 32 + lr, c)]);
+        af[i] = __builtin_bit_cast(bf16x8, As[cur][swz<kChunks>(wm * WTM + i * 32 + lr, c)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][swz(wn * WTN + j * 32 + lr, c)]);
+        bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][swz<kChunks>(wn * WTN + j * 32 + lr, c)]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -206,7 +222,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int gemm1_impl(const void* x, const void* w, const int32_t* sorted_ids, const int32_t* expert_of_block,
                const int32_t* num_post_pad, int M, int k, int E, int K, int N, int block, void* y,
                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (M < 0 || k < 1 || k > 64 || E < 1 || E > 4096 || K <= 0 || K % kBK != 0 || N <= 0 ||
+  if (M < 0 || k < 1 || k > 64 || E < 1 || E > 4096 || K <= 0 || K % kKAlign != 0 || N <= 0 ||
       N % 128 != 0 || block < 32 || block % 32 != 0)
     return MRS_ERR_INVALID_ARG;
   if (!x || !w || !sorted_ids || !expert_of_block || !num_post_pad || !y) return MRS_ERR_NULL_POINTER;
