@@ -87,13 +87,15 @@ def to_gpu(inp, torch):
 EXTRA_STEPS = 250
 
 
-def graph_size(steps, cap=100):
+def graph_size(steps, cap=100, min_samples=5):
     """Calls per captured graph: the largest divisor of `steps` not above
-    `cap` or steps / 5, so a run has at least five samples (replays).  A
+    `cap` or steps / min_samples, so a run has at least that many replays.  A
     replay must hold enough GPU work that the host's replay submission does
     not pace the GPU: an empty one-workgroup kernel measured 4.6 us per call
-    at 10 calls per replay, 2.0 at 20, 1.7 at 50 and 1.6 at 100."""
-    cap = max(1, min(cap, steps // 5))
+    at 10 calls per replay, 2.0 at 20, 1.7 at 50 and 1.6 at 100; the 8192 x
+    896 call 22.6 us at 4 calls per replay with an event between replays,
+    21.5 without the events, 20.8 at 20 calls and 20.1 at 100."""
+    cap = max(1, min(cap, steps // min_samples))
     return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
 
 
@@ -113,19 +115,36 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     with torch.cuda.stream(stream):
         out = amr.route_sort(x0, b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block)
     torch.cuda.synchronize()
-    # The timed steps replay a HIP graph of G consecutive calls (rotating inputs),
-    # so host-side launch overhead does not pace the GPU.
-    G = graph_size(steps)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(G):
-            amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
-    torch.cuda.synchronize()
+    # The timed steps replay a HIP graph of consecutive calls (rotating
+    # inputs), so host-side launch overhead does not pace the GPU.
+    def capture(G):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(G):
+                amr.route_sort(xs[i % nrot], b, cfg.k, cfg.n_group, cfg.topk_group, cfg.block, out=out)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, warmup // G)):
+                graph.replay()
+        torch.cuda.synchronize()
+        return graph
+    # The value: exactly `steps` calls in graphs of up to 100 calls, events at
+    # the two ends only (an event between replays costs time of its own).
+    Gv = graph_size(steps, min_samples=1)
+    graph = capture(Gv)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
     with torch.cuda.stream(stream):
-        for _ in range(max(1, warmup // G)):
+        for i in range(steps // Gv):
             graph.replay()
+    end.record(stream)
     torch.cuda.synchronize()
-    # events between the replays split the timed steps into samples of G calls
+    ms = start.elapsed_time(end) / steps
+    del graph
+    # The spread: another `steps` calls, split by events into at least five
+    # samples of G calls (smaller graphs, so these samples run a little slower)
+    G = graph_size(steps)
+    graph = capture(G)
     nrep = steps // G
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
     marks[0].record(stream)
@@ -134,7 +153,7 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
             graph.replay()
             marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = marks[0].elapsed_time(marks[-1]) / (nrep * G)
+    del graph
     per_call = np.array([marks[i].elapsed_time(marks[i + 1]) / G for i in range(nrep)]) * 1e3  # us
     npp = int(out.num_post_pad.item())
     # host wall time per call, launch + synchronise (latency view)
@@ -148,7 +167,7 @@ def time_workload(cfg, steps, warmup, rotate_mb, torch, amr, per_kernel=False):
     nbytes = algorithmic_bytes(cfg, npp)
     r = dict(ms=ms, npp=npp, nbytes=nbytes, rot=nrot, wall_us=wall_us,
              routes_per_s=cfg.M * cfg.k / (ms * 1e-3), gbps=nbytes / (ms * 1e-3) / 1e9,
-             samples=nrep, calls_per_sample=G,
+             value_calls_per_graph=Gv, samples=nrep, calls_per_sample=G,
              us_per_call_p10_p50_p90=[round(float(v), 3) for v in np.percentile(per_call, [10, 50, 90])])
     if per_kernel:
         # HIP events stamped with each kernel's own start and end by the
@@ -653,7 +672,8 @@ def main():
         "us_per_call": r["ms"] * 1e3,
         "us_per_call_p10_p50_p90": r["us_per_call_p10_p50_p90"],
         "warm_us_per_call": rw["ms"] * 1e3,
-        "timing": {"graph_calls_per_sample": r["calls_per_sample"], "samples": r["samples"]},
+        "timing": {"value_graph_calls": r["value_calls_per_graph"], "spread_graph_calls": r["calls_per_sample"],
+                   "spread_samples": r["samples"]},
         "launches_per_call": r["launches"],
         "decode_us_per_call": extra.get("decode", {}).get("us_per_call"),
         "hbm_copy_gbps_measured": copy_gbps,
