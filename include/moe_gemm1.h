@@ -30,9 +30,11 @@
  * Requirements: K > 0 and K % 64 == 0; N > 0 and N % 128 == 0; block >= 32 and
  * block % 32 == 0 (a tile of rows never spans two experts); x, w, y 16-byte
  * aligned.  Returns 0 or a negative MRS_ERR_* code (moe_route_sort.h) before
- * any launch.  A block whose expert id lies outside [0, E) and rows whose slot
- * lies outside [0, M*k) are treated as not routed (no row of x or W is read
- * for them).  Asynchronous on `stream`; allocates nothing; one launch.
+ * any launch.  Rows whose slot lies outside [0, M*k) are padding and are
+ * written as zeros (their load reads row 0 of x and discards it).  A tile
+ * whose block's expert id lies outside [0, E) reads no weights and writes
+ * nothing (metadata from moe_route_sort never holds one).  Asynchronous on
+ * `stream`; allocates nothing; one launch.
  */
 #ifndef MOE_GEMM1_H_
 #define MOE_GEMM1_H_
