@@ -16,7 +16,9 @@
  *               kept, ties to the lower group index
  *   out_ids   = the k best keys inside the kept groups, ties to the lower
  *               expert index, listed in ascending expert id
- *   out_w     = s[t,id] / sum of s over the k picks (unbiased scores)
+ *   out_w     = s[t,id] / sum of s over the k picks (unbiased scores); the
+ *               sum is formed in float64 and the returned FP32 weight lies
+ *               within 2^-22 (relative) of the exact quotient
  *   slot      = t*k + j; sentinel = M*k
  *   count[e]  = number of slots routed to e (phase 1: histogram)
  *   padded[e] = ceil(count[e] / block) * block
