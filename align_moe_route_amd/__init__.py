@@ -208,7 +208,7 @@ def route_sort(logits, bias, k: int, n_group: int, topk_group: int, block: int, 
             first call on a stream before capturing a graph on it, or the
             allocation and zero fill of that buffer join the graph.
     stats:  optional int32 [3] device tensor (tokens decided by the workgroup-wide
-            exact selection / by one wave / redone with exact keys by one wave).
+            exact selection / by one wave / with group scores made exact by one wave).
     events: optional list of 6 torch.cuda.Event(enable_timing=True); events
             2i and 2i+1 take the start and end of the call's kernel i (pairs
             past the last kernel are recorded after it); returns

@@ -26,9 +26,9 @@
 //   2. group stage: each group's top two merged across its lanes with DPP,
 //      group score, rank of every group by (score desc, index asc) by counting
 //      in LDS.  With fast keys the kept set is accepted only if it beats the
-//      dropped groups by more than the fast scores' error, else the token is
-//      redone by its wave with correctly rounded keys (in place, or after the
-//      wave's last token when the row lives in the key registers);
+//      dropped groups by more than the fast scores' error; otherwise the wave
+//      computes correctly rounded keys for the few experts that can be among
+//      their group's top two, which makes the group scores exact;
 //   3. threshold: a lower bound of the k-th largest of the kept lanes' top-two
 //      keys (at least k keys reach it), by ballot-count bisection over the
 //      highest differing bits; with fast keys it is lowered by 2*delta;
@@ -90,7 +90,7 @@ enum { KIND_SMALL = 0, KIND_SELECT = 1, KIND_SCATTER = 2 };
 // LOAD_KEYS: the whole workgroup computes every exact key (and score) of the
 // batch into LDS first; the waves then select from them (small batches)
 enum { LOAD_VEC = 0, LOAD_STAGE = 1, LOAD_KEYS = 2 };
-enum { TOK_DONE = 0, TOK_REDO_EXACT = 1, TOK_ESCALATE = 2 };
+enum { TOK_DONE = 0, TOK_ESCALATE = 1 };
 
 struct Args {
   const void* logits;
@@ -613,6 +613,25 @@ struct Ownership {
   }
 };
 
+// Largest and second largest correctly rounded key over the register slots
+// in rm of a lane (slot i holds expert own.expert(i)); x = the token's row.
+__device__ __forceinline__ float2 exact_top2(const float* x, const float* bias, unsigned long long rm,
+                                                       Ownership own) {
+  float e1 = -INFINITY, e2 = -INFINITY;
+  while (rm) {
+    const int e = own.expert((int)__builtin_ctzll(rm));
+    rm &= rm - 1;
+    bool amb;
+    float up;
+    float s = sigrn::sigmoid_rn32_try(x[e], amb, up);
+    if (amb) s = sigmoid_settle(x[e], s, up);
+    const float key = s + bias[e];
+    e2 = __builtin_amdgcn_fmed3f(e1, e2, key);
+    e1 = __builtin_amdgcn_fmed3f(e1, key, INFINITY);
+  }
+  return make_float2(e1, e2);
+}
+
 // s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N), N < 64
@@ -729,9 +748,9 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
 // One token per segment (see the header comment).  BF16 logits take their
 // correctly rounded sigmoid from the LDS table, so every key is exact and one
 // pass decides the token.  FP32 logits rank with sigmoid_fast: the group
-// boundary is certified against the error of the fast scores (else the token
-// is redone with `exact` keys) and the candidate line is lowered by twice the
-// key error.  Written for a short instruction stream: compile-time layout,
+// boundary is certified against the error of the fast scores (else the group
+// scores are made exact in place) and the candidate line is lowered by twice
+// the key error.  Written for a short instruction stream: compile-time layout,
 // table offsets with packed 16-bit arithmetic, straight-line group and
 // threshold stages.  LPG > 0 fixes the lanes per group at compile time (the
 // group stage then has no run-time branches or loop bounds); LPG == 0 reads
@@ -745,8 +764,7 @@ __device__ __forceinline__ unsigned long long seg_bits(unsigned long long bal, i
 // half of its next token's row (`next_t`) into `av`, after the candidates'
 // own logits, so that the transfer overlaps the ranking and output steps and
 // the next token starts on data already in flight (`have_row`; it requests
-// the second half itself).  A token to be redone with exact keys is redone
-// after the wave's last token, by a pass that loads its whole row again.
+// the second half itself).
 template <int SEG, int EPL, bool BF16, int MODE>
 constexpr bool row_in_keys() {
   return !BF16 && MODE == LOAD_VEC && SEG == 64 && (EPL == 0 || EPL > 32);
@@ -771,10 +789,13 @@ __device__ __forceinline__ void load_row_vec(const Args& a, size_t row, int e_sl
 
 template <int SEG, int EPL, bool BF16, int MODE, int LPG = 0>
 __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act, int t, int tl,
-                                          const unsigned char* stage, const float* bv, double delta,
-                                          double epsg, bool exact, float (&av)[EPL > 0 ? EPL : 64],
-                                          bool have_row, int next_t) {
-  if (BF16 || MODE == LOAD_KEYS) exact = true;
+                                          const unsigned char* stage, const float* bv, float d2, float e2,
+                                          float (&av)[EPL > 0 ? EPL : 64], bool have_row,
+                                          int next_t) {
+  // BF16 keys (from the table) and precomputed keys are exact; FP32 logits
+  // give fast keys, within delta of the exact ones (d2 >= 2 delta and e2 >= 2
+  // epsg are those bounds as floats, rounded up)
+  constexpr bool exact = BF16 || MODE == LOAD_KEYS;
   constexpr int NSEG = kWave / SEG;
   constexpr int EPLM = EPL > 0 ? EPL : 64;
   constexpr bool RIK = row_in_keys<SEG, EPL, BF16, MODE>();
@@ -807,23 +828,7 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
     put_key(i, sig_lds(o0) + bias_of(i));
     put_key(i + 1, sig_lds(o1) + bias_of(i + 1));
   };
-  // exact keys: RN32 of the float64 sigmoid.  A quotient that lies near an
-  // FP32 rounding midpoint makes the key +inf (no real key is infinite); the
-  // token is then sent to the workgroup path, which settles it exactly, and
-  // the double-double settlement stays out of this unrolled loop
-  auto put = [&](int i, float x) {  // FP32 logit of expert i
-    float s;
-    if (exact) {
-      bool amb;
-      float up;
-      s = sigrn::sigmoid_rn32_try(x, amb, up);
-      s = amb ? INFINITY : s;
-    } else {
-      s = sigmoid_fast(x);
-    }
-    put_key(i, s + bias_of(i));
-    if (exact) __builtin_amdgcn_sched_barrier(0);  // one float64 sigmoid live at a time
-  };
+  auto put = [&](int i, float x) { put_key(i, sigmoid_fast(x) + bias_of(i)); };  // FP32 logit of expert i
   if (EPL == 0 && !RIK) {  // slots past epl stay defined (their candidate bits are masked off)
 #pragma unroll
     for (int i = 0; i < EPLM; ++i) av[i] = 0.0f;
@@ -928,50 +933,80 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
 
   // ---- 2. group stage ----
   bool allowed = act;
-  bool redo = false;
   if (a.gstage) {
     constexpr int LG = LPG == 1 ? 0 : LPG == 2 ? 1 : LPG == 4 ? 2 : LPG == 8 ? 3 : LPG == 16 ? 4 : LPG == 32 ? 5 : -1;
     static_assert(LPG == 0 || LG >= 0, "lanes per group: a power of two up to 32");
     const int lg_lpg = LPG ? LG : a.lg_lpg;
     const int ngs = LPG ? SEG / LPG : a.n_group;  // groups in a segment (n_group)
-    float g1 = lm, g2 = l2;
-#pragma unroll
-    for (int lev = 0; lev < (SEG == 64 ? 5 : 4); ++lev) {
-      if (lev < lg_lpg) {  // wave-uniform
-        // merge two (largest, second largest) pairs: the new second largest is
-        // the median of both largest values and the larger second value
-        const float p1 = butterfly_partner(g1, lev);
-        const float p2 = butterfly_partner(g2, lev);
-        g2 = __builtin_amdgcn_fmed3f(g1, p1, __builtin_amdgcn_fmed3f(g2, p2, INFINITY));
-        g1 = __builtin_amdgcn_fmed3f(g1, p1, INFINITY);
-      }
-    }
-    const uint32_t gsu = f2s(g1 + g2);
     const int g = ls >> lg_lpg;
-    const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
     unsigned long long* gc = L.gcomp + w * kWave + seg * SEG;
-    if ((ls & ((1 << lg_lpg) - 1)) == 0) gc[g] = cg;
-    wave_sync_lds();
-    int rank = 0;
-    if constexpr (LPG > 0) {
+    // (largest, second largest) of the group in every lane of the group
+    auto merge = [&](float& g1, float& g2) {
 #pragma unroll
-      for (int h = 0; h < SEG / LPG; ++h) rank += (gc[h] > cg ? 1 : 0);
-    } else {
-      for (int h = 0; h < ngs; h += 2) {  // n_group is even here
-        const unsigned long long c0 = gc[h], c1 = gc[h + 1];
-        rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
+      for (int lev = 0; lev < (SEG == 64 ? 5 : 4); ++lev) {
+        if (lev < lg_lpg) {  // wave-uniform
+          // merge two (largest, second largest) pairs: the new second largest is
+          // the median of both largest values and the larger second value
+          const float p1 = butterfly_partner(g1, lev);
+          const float p2 = butterfly_partner(g2, lev);
+          g2 = __builtin_amdgcn_fmed3f(g1, p1, __builtin_amdgcn_fmed3f(g2, p2, INFINITY));
+          g1 = __builtin_amdgcn_fmed3f(g1, p1, INFINITY);
+        }
+      }
+    };
+    // rank of the lane's group by (score desc, index asc), counted over the
+    // (score, ~group) composites of the segment
+    auto rank_of = [&](uint32_t gsu) {
+      const unsigned long long cg = ((unsigned long long)gsu << 32) | (uint32_t)(0xFFFFu - g);
+      if ((ls & ((1 << lg_lpg) - 1)) == 0) gc[g] = cg;
+      wave_sync_lds();
+      int rank = 0;
+      if constexpr (LPG > 0) {
+#pragma unroll
+        for (int h = 0; h < SEG / LPG; ++h) rank += (gc[h] > cg ? 1 : 0);
+      } else {
+        for (int h = 0; h < ngs; h += 2) {  // n_group is even here
+          const unsigned long long c0 = gc[h], c1 = gc[h + 1];
+          rank += (c0 > cg ? 1 : 0) + (c1 > cg ? 1 : 0);
+        }
+      }
+      return rank;
+    };
+    float g1 = lm, g2 = l2;
+    merge(g1, g2);
+    uint32_t gsu = f2s(g1 + g2);
+    int rank = rank_of(gsu);
+    if (!exact) {
+      // The kept groups' lowest score must beat the others' highest by more
+      // than the error of two fast group scores.  Otherwise the group scores
+      // are made exact: an expert whose fast key is below its group's fast
+      // second largest minus 2 delta has an exact key below the group's exact
+      // second largest (at least two experts reach the fast second largest
+      // minus delta exactly), so only the experts at or above that bound
+      // -- typically the group's top two -- need a correctly rounded key.
+      const bool keep0 = rank < a.topk_group;
+      const uint32_t kept_min = seg_min_u32<SEG>(keep0 ? gsu : 0xFFFFFFFFu);
+      const uint32_t drop_max = seg_max_u32<SEG>(keep0 ? 0u : gsu);
+      // next_down of the rounded difference is at most the exact one
+      const float gap = next_down(s2f(kept_min) - s2f(drop_max));
+      const bool need = act && !(gap > e2);  // uniform in the segment
+      if (__ballot(need)) {  // wave-uniform
+        const float c2 = next_down(g2 - d2);
+        MaskT rm = 0;
+#pragma unroll
+        for (int i = 0; i < EPLM; ++i)
+          if ((EPL > 0 || i < epl) && av[i] >= c2) rm |= (MaskT)1 << i;
+        if (!need) rm = 0;
+        const float2 et = exact_top2(reinterpret_cast<const float*>(a.logits) + row, L.bias, rm, own);
+        float e1 = et.x, e2 = et.y;
+        merge(e1, e2);
+        if (need) gsu = f2s(e1 + e2);
+        wave_sync_lds();  // every lane has read the fast composites
+        rank = rank_of(gsu);
+        if (a.stats && need && ls == 0) atomicAdd(&L.misc[3], 1);
       }
     }
-    const bool keep = rank < a.topk_group;
-    if (!exact) {
-      // the kept groups' lowest score must beat the others' highest by more
-      // than the error of two fast group scores
-      const uint32_t kept_min = seg_min_u32<SEG>(keep ? gsu : 0xFFFFFFFFu);
-      const uint32_t drop_max = seg_max_u32<SEG>(keep ? 0u : gsu);
-      const double gap = (double)s2f(kept_min) - (double)s2f(drop_max);
-      redo = !(gap > 2.0 * epsg);
-    }
-    allowed = act && keep;
+    allowed = act && rank < a.topk_group;
     wave_sync_lds();  // every lane has read the composites before step 5 reuses the space
   }
 
@@ -1013,10 +1048,9 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   }
   const uint32_t T = (NSEG == 1 || seg == 0) ? Ts[0] : Ts[NSEG - 1];
   float thr = s2f(T);
-  if (!exact) thr = next_down((float)((double)thr - 2.0 * delta));
+  if (!exact) thr = next_down(thr - d2);
   const bool ok = (NSEG == 1 || seg == 0) ? okseg[0] : okseg[NSEG - 1];
-  const bool amb_seg = exact && !BF16 && MODE != LOAD_KEYS && seg_max_u32<SEG>(f2s(lm)) == f2s(INFINITY);
-  int status = !act ? TOK_ESCALATE : ((!ok || amb_seg) ? TOK_ESCALATE : (redo ? TOK_REDO_EXACT : TOK_DONE));
+  int status = (act && ok) ? TOK_DONE : TOK_ESCALATE;
 
   // ---- 4. candidates (keys >= thr), compacted in expert order ----
   // The sign of key - thr is 1 exactly when key < thr (keys are never -0 and a
@@ -1203,7 +1237,8 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   }
   if (tid == 0) {
     L.misc[0] = 0;  // tokens for the workgroup-wide exact selection
-    L.misc[3] = 0;  // tokens redone with exact keys by their wave (statistics)
+    L.misc[3] = 0;  // tokens whose group scores were made exact by their wave (statistics)
+    L.misc[4] = kNW * NSEG;  // next token to claim (row-in-registers loop)
   }
   if constexpr (MODE == LOAD_KEYS) {
     // every exact key and score of the batch, one (token, expert) per thread
@@ -1300,49 +1335,55 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
     const double B = 1.0 + (double)__uint_as_float(wave_max_u32(__float_as_uint(bmax))) + 0x1p-20;
     const double delta = 0x1p-21 + (B + 1.0) * 0x1p-23;
     const double epsg = 2.0 * delta + (2.0 * B + 1.0) * 0x1p-23;
-    unsigned long long redo_rounds = 0;  // rounds whose token is redone with exact keys (RIK)
-    for (int it = 0; (it * kNW + w) * NSEG < nt; ++it) {
-      const int tl = tok_of(it);
-      const int tn = ((it + 1) * kNW + w) * NSEG < nt ? t0 + tok_of(it + 1) : -1;
-      const int cb = a.nbuf > 1 ? (it & 1) : 0;
-      const unsigned char* cur = stg + (size_t)(cb * NSEG + seg) * sb;
-      if (MODE == LOAD_STAGE) {
-        wait_vmem_all();  // this round's rows have landed in LDS
-        // the host gives two buffers whenever a wave has a next round
-        if (a.nbuf > 1 && ((it + 1) * kNW + w) * NSEG < nt) {
-          const int tn = tok_of(it + 1);
-          stage_rows_async<SEG, EPL>(a, stg + (size_t)(cb ^ 1) * NSEG * sb, sb, tn < 0 ? -1 : t0 + tn, BF16 ? 2 : 4);
+    auto up_f = [](double x) {  // the least float >= x > 0, in a scalar register
+      const float f = (float)x;
+      const uint32_t u = __float_as_uint(f) + ((double)f < x ? 1u : 0u);
+      return __uint_as_float(__builtin_amdgcn_readfirstlane(u));
+    };
+    const float d2 = up_f(2.0 * delta), e2 = up_f(2.0 * epsg);
+    if constexpr (RIK) {
+      // One token per wave at a time, taken from a workgroup counter: a wave
+      // that the SIMD's issue order favours takes more tokens, so the waves of
+      // a workgroup finish together (with four tokens each, the last wave of a
+      // workgroup ended 12-17 us after the first on the 16384 x 4096
+      // workload).  The first token is w (its first half-row was requested
+      // above); the next is claimed before the current one starts, so that
+      // its first half-row can be prefetched.
+      int tl = w;
+      while (tl < nt) {  // wave-uniform
+        int nx = 0;
+        if (ls == 0) nx = atomicAdd(&L.misc[4], 1);
+        nx = __builtin_amdgcn_readfirstlane(nx);
+        const int st =
+            lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, true, t0 + tl, tl, stg, bv, d2, e2, av, true,
+                                                  nx < nt ? t0 + nx : -1);
+        if (st == TOK_ESCALATE && ls == 0) {
+          const int q = atomicAdd(&L.misc[0], 1);
+          L.esc[q] = tl;
         }
+        tl = nx;
       }
-      const bool act = tl >= 0;
-      int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, act, t0 + tl, tl, cur, bv, delta, epsg, false, av, RIK, tn);
-      if (RIK) {
-        // one token per wave: a token to redo is only noted here, and redone
-        // after the loop, so the exact pass does not share the loop's registers
-        if (__ballot(act && st == TOK_REDO_EXACT)) redo_rounds |= 1ull << it;
-        st = st == TOK_REDO_EXACT ? TOK_DONE : st;
-      } else if (!BF16 && __ballot(act && st == TOK_REDO_EXACT)) {
-        const bool redo = act && st == TOK_REDO_EXACT;
-        if (a.stats && redo && ls == 0) atomicAdd(&L.misc[3], 1);
-        const int st2 =
-            lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, redo, t0 + tl, tl, cur, bv, delta, epsg, true, av, false, tn);
-        if (redo) st = st2;
-      }
-      if (act && st == TOK_ESCALATE && ls == 0) {
-        const int q = atomicAdd(&L.misc[0], 1);
-        L.esc[q] = tl;
-      }
-    }
-    while (RIK && redo_rounds) {  // wave-uniform
-      const int it = __builtin_ctzll(redo_rounds);
-      redo_rounds &= redo_rounds - 1;
-      const int tl = tok_of(it);
-      if (a.stats && ls == 0) atomicAdd(&L.misc[3], 1);
-      const int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, true, t0 + tl, tl, stg, bv, delta, epsg, true, av,
-                                                           false, -1);
-      if (st == TOK_ESCALATE && ls == 0) {
-        const int q = atomicAdd(&L.misc[0], 1);
-        L.esc[q] = tl;
+    } else {
+      for (int it = 0; (it * kNW + w) * NSEG < nt; ++it) {
+        const int tl = tok_of(it);
+        const int tn = ((it + 1) * kNW + w) * NSEG < nt ? t0 + tok_of(it + 1) : -1;
+        const int cb = a.nbuf > 1 ? (it & 1) : 0;
+        const unsigned char* cur = stg + (size_t)(cb * NSEG + seg) * sb;
+        if (MODE == LOAD_STAGE) {
+          wait_vmem_all();  // this round's rows have landed in LDS
+          // the host gives two buffers whenever a wave has a next round
+          if (a.nbuf > 1 && ((it + 1) * kNW + w) * NSEG < nt) {
+            const int tn = tok_of(it + 1);
+            stage_rows_async<SEG, EPL>(a, stg + (size_t)(cb ^ 1) * NSEG * sb, sb, tn < 0 ? -1 : t0 + tn,
+                                       BF16 ? 2 : 4);
+          }
+        }
+        const bool act = tl >= 0;
+        const int st = lean_token<SEG, EPL, BF16, MODE, LPG>(a, L, act, t0 + tl, tl, cur, bv, d2, e2, av, false, tn);
+        if (act && st == TOK_ESCALATE && ls == 0) {
+          const int q = atomicAdd(&L.misc[0], 1);
+          L.esc[q] = tl;
+        }
       }
     }
   } else {

@@ -135,10 +135,11 @@ enum {
  * moe_route_sort_ex -- moe_route_sort with option bits and optional device
  * statistics.  `stats`, when not NULL, is device int32[3] that the call
  * increments: stats[0] += tokens decided by the workgroup-wide exact selection,
- * stats[1] += tokens decided by one wave, stats[2] += tokens that one wave
- * redid with exact keys because the fast (FP32) keys left the group boundary
- * uncertain (each also counts in stats[0] or stats[1], wherever it was
- * decided).  Unknown flag bits or a forced path that cannot take the shape
+ * stats[1] += tokens decided by one wave, stats[2] += tokens whose group
+ * scores one wave made exact (correctly rounded keys for the experts that can
+ * be among their group's top two) because the fast (FP32) keys left the group
+ * boundary uncertain (each also counts in stats[0] or stats[1], wherever it
+ * was decided).  Unknown flag bits or a forced path that cannot take the shape
  * return MRS_ERR_INVALID_ARG.
  */
 int moe_route_sort_ex(const void* logits, const float* bias, int M, int E, int k, int n_group,

@@ -83,7 +83,7 @@ def test_workload_parity(name):
     stats = torch.zeros(3, dtype=torch.int32, device="cuda")
     g = run(inp, stats=stats)
     st = stats.cpu().numpy()
-    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, redone in the wave {st[2]}", flush=True)
+    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, exact group scores {st[2]}", flush=True)
     assert st[0] + st[1] == cfg.M
     assert_parity(inp, g)
 
@@ -155,7 +155,7 @@ SWEEP = [
     (80, 4096, 8, 32, 10, 32, "f32", "shared"),       # 2-lane groups, 4-lane blocks
     # FP32 rows in the key registers with the next row requested early, two
     # tokens per wave: runs of 20 and 40 experts (run-time length), and pairs
-    # of equal keys (group boundaries redone with exact keys after the loop)
+    # of equal keys (group scores made exact in the wave)
     (5000, 1280, 16, 4, 2, 64, "f32", "normal"),
     (5000, 2560, 16, 8, 4, 64, "f32", "duplicated"),
     # small batches with the keys computed by the whole workgroup up front
@@ -481,30 +481,31 @@ def test_stats_count_every_token():
     run(inp, stats=stats)
     run(inp, flags=amr.FLAG_FORCE_EXACT, stats=stats)
     st = stats.cpu().numpy()
-    assert st[0] + st[1] == 2 * cfg.M and st[0] >= cfg.M and st[2] == 0  # BF16: never redone
+    assert st[0] + st[1] == 2 * cfg.M and st[0] >= cfg.M and st[2] == 0  # BF16 keys are exact already
 
 
 @pytest.mark.parametrize("case", [
-    # FP32 rows in the key registers, two tokens per wave: redone after the loop
+    # FP32 rows in the key registers, tokens claimed one at a time by each wave
     (5000, 2560, 16, 8, 4, 64, "f32", "duplicated"),
-    # 32-lane segments (two tokens per wave): redone in place
+    # 32-lane segments (two tokens per wave)
     (5000, 896, 16, 8, 4, 128, "f32", "equal"),
-    # one token per wave, rows staged in LDS (14 experts per lane): redone in place
+    # one token per wave, rows staged in LDS (14 experts per lane)
     (200, 896, 16, 8, 4, 32, "f32", "equal"),
 ], ids=lambda c: "M{}_E{}".format(c[0], c[1]))
-def test_exact_redo_in_the_wave(case):
+def test_exact_group_scores_in_the_wave(case):
     """Equal group scores (pairs of identical keys; all keys equal) leave the
-    group boundary of the fast keys uncertain, so the wave redoes those
-    tokens with exact keys: the redo paths are taken, and every token still
-    matches the oracle (with all keys equal the exact pass then hands the
-    token to the workgroup-wide selection)."""
+    group boundary of the fast keys uncertain, so the wave makes those
+    tokens' group scores exact: the refinement is taken on every layout, and
+    every token still matches the oracle (with all keys equal the candidates
+    then outnumber the lanes and the token goes to the workgroup-wide
+    selection)."""
     M, E, k, ng, tg, block, dtype, dist = case
-    print(f"[gpu] exact redo M={M} E={E} {dtype} {dist}", flush=True)
+    print(f"[gpu] exact group scores M={M} E={E} {dtype} {dist}", flush=True)
     inp = workloads.make_inputs(workloads.custom(M, E, k, ng, tg, block, dtype, dist, seed=3))
     stats = torch.zeros(3, dtype=torch.int32, device="cuda")
     g = run(inp, stats=stats)
     st = stats.cpu().numpy()
-    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, redone in the wave {st[2]}", flush=True)
+    print(f"  exact-path tokens {st[0]}, fast-path tokens {st[1]}, exact group scores {st[2]}", flush=True)
     assert st[0] + st[1] == M
     assert st[2] > 0
     assert_parity(inp, g)
