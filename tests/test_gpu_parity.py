@@ -153,11 +153,14 @@ SWEEP = [
     (90, 4096, 16, 8, 3, 64, "f32", "hot"),           # 8-lane groups, 16-lane blocks
     (75, 4096, 16, 16, 8, 128, "f32", "coarse"),      # 4-lane groups, 8-lane blocks, many exact ties
     (80, 4096, 8, 32, 10, 32, "f32", "shared"),       # 2-lane groups, 4-lane blocks
-    # FP32 rows in the key registers with the next row requested early, two
-    # tokens per wave: runs of 20 and 40 experts (run-time length), and pairs
-    # of equal keys (group scores made exact in the wave)
+    # FP32 rows in the key registers with the next row requested early, the
+    # tokens claimed by the waves: runs of 20 and 40 experts (run-time
+    # length), and pairs of equal keys (group scores made exact in the wave)
     (5000, 1280, 16, 4, 2, 64, "f32", "normal"),
     (5000, 2560, 16, 8, 4, 64, "f32", "duplicated"),
+    # 20 tokens per workgroup (four claimed after the first sixteen) and a
+    # last workgroup of 4 tokens (twelve waves without a token)
+    (4984, 4096, 16, 16, 8, 128, "f32", "normal"),
     # small batches with the keys computed by the whole workgroup up front
     (2, 896, 16, 8, 4, 32, "bf16", "shared"),         # 14 experts per lane, 8 lanes per group fixed
     (16, 128, 8, 4, 2, 16, "f32", "equal"),           # one token per wave, all keys equal
