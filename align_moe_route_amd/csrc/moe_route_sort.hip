@@ -76,11 +76,15 @@ constexpr int kEMax = 4096;              // 16 KiB of 32-bit counters, the pages
 constexpr int kKeysPreMax = 2048;        // small batches with at most this many keys precompute them
 constexpr int kBiasRegMax = 32;          // lanes keep their biases in registers up to this many experts
 // Correctly rounded sigmoid of every BF16 value, 8192 FP32 entries: entry
-// 2t + s is the value at the BF16 pattern (0x3300 + t) | s << 15.  Below the
-// window (|x| < 2^-25) the sigmoid rounds to 0.5, above it (|x| >= 128) to 1
-// or 0, so clamping t into [0, 4095] gives the exact value for every BF16 x.
+// 4096 s + t is the value at the BF16 pattern (0x3300 + t) | s << 15.  Below
+// the window (|x| < 2^-25) the sigmoid rounds to 0.5, above it (|x| >= 128)
+// to 1 or 0, so clamping t into [0, 4095] gives the exact value for every
+// BF16 x.  In LDS the negative half starts at byte 32768, so that the sign
+// bit of a pattern is already the sign bit of its entry's byte offset
+// (4 t + 32768 s): 48 KiB, of which bytes [16384, 32768) hold no entry.
 constexpr int kSigEntries = 8192;
-constexpr int kSigBytes = kSigEntries * 4;
+constexpr int kSigBytes = kSigEntries * 4;     // the table in global memory
+constexpr int kSigLdsBytes = 3 * kSigBytes / 2;  // its LDS image
 constexpr uint32_t kSigBase = 0x3300;
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kWsHeader = 256;
@@ -154,7 +158,7 @@ __host__ __device__ inline LdsPlan lds_plan(int kind, int E, int n_group, int gs
   LdsPlan p{};
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o = (o + n + 15) & ~(size_t)15; return r; };
-  if (kind != KIND_SCATTER && tbl) p.sig = take(kSigBytes);  // at LDS offset 0
+  if (kind != KIND_SCATTER && tbl) p.sig = take(kSigLdsBytes);  // at LDS offset 0
   if (kind != KIND_SCATTER) p.bits = take((size_t)E * 8);
   p.redd = take((size_t)kNW * 8);
   if (kind != KIND_SELECT) p.off = take((size_t)E * 4);
@@ -308,24 +312,27 @@ __device__ __forceinline__ const float* sig_table_copy(const float* base, int wg
 }
 
 
-// Byte offset of a BF16 pattern's entry: 8 * clamp(|h| - base, 0, 4095) + 4 * sign.
+// LDS byte offset of a BF16 pattern's entry: 4 * clamp(|h| - base, 0, 4095)
+// + 32768 * sign (the pattern's own sign bit, in place).
 __device__ __forceinline__ uint32_t sig_off1(uint32_t h) {
   const int t = (int)(h & 0x7FFFu) - (int)kSigBase;
   const uint32_t c = (uint32_t)min(max(t, 0), 4095);
-  return (c << 3) | ((h >> 13) & 4u);
+  return (c << 2) | (h & 0x8000u);
 }
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // Both entries of a pair of BF16 patterns packed in one word (low half first),
-// with packed 16-bit integer arithmetic.
+// with packed 16-bit integer arithmetic; the sign bits stay where they are.
 __device__ __forceinline__ void sig_off2(uint32_t d, uint32_t& o0, uint32_t& o1) {
   u16x2 m = __builtin_bit_cast(u16x2, d & 0x7FFF7FFFu);
   m = __builtin_elementwise_sub_sat(m, (u16x2){(unsigned short)kSigBase, (unsigned short)kSigBase});
   m = __builtin_elementwise_min(m, (u16x2){4095, 4095});
-  m = m << (u16x2){3, 3};
-  const uint32_t v = __builtin_bit_cast(uint32_t, m) | ((d >> 13) & 0x00040004u);
-  o0 = v & 0xFFFFu;
+  m = m << (u16x2){2, 2};
+  const uint32_t v = __builtin_bit_cast(uint32_t, m) | (d & 0x80008000u);  // one v_and_or_b32
+  o0 = __builtin_amdgcn_perm(0u, v, 0x0C0C0100u);  // bytes 0-1 of v (a byte permute keeps the and-or whole)
   o1 = v >> 16;
 }
+// LDS float index of table entry j (the negative half starts at byte 32768)
+__host__ __device__ constexpr int sig_lds_index(int j) { return (j & 4095) + (j >> 12) * 8192; }
 // The table sits at LDS address 0 (the kernels that use it have no static
 // LDS, so their dynamic LDS starts there; the host checks this), which lets
 // the byte offset serve directly as the LDS address.
@@ -1205,10 +1212,12 @@ __device__ void select_tokens(const Args& a, const Lds& L, int t0, int nt) {
   }
   if (a.tbl) {
     const unsigned char* src = reinterpret_cast<const unsigned char*>(sig_table_copy(a.sigtab, blockIdx.x));
+    // 16 KiB per pass: the positive half to LDS byte 0, the negative half to 32768
+    static_assert(kWG * 16 * 2 == kSigBytes, "two passes over the table");
 #pragma unroll
-    for (int j = 0; j * kWG * 16 < kSigBytes; ++j)
+    for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_global_load_lds(src + (size_t)(j * kWG + tid) * 16,
-                                       (__attribute__((address_space(3))) void*)(size_t)(j * kWG * 16 + wbase), 16,
+                                       (__attribute__((address_space(3))) void*)(size_t)(j * 32768 + wbase), 16,
                                        0, 0);
   }
   if (MODE != LOAD_KEYS && a.bias_dma) {  // precomputed keys already hold the bias
@@ -1950,7 +1959,7 @@ __global__ __launch_bounds__(256) void k_sigmoid_table_probe(const float* table,
                                                              float* o2) {
   float* tab = reinterpret_cast<float*>(g_lds);
   const float* src = sig_table_copy(table, blockIdx.x);
-  for (int j = threadIdx.x; j < kSigEntries; j += 256) tab[j] = src[j];
+  for (int j = threadIdx.x; j < kSigEntries; j += 256) tab[sig_lds_index(j)] = src[j];
   __syncthreads();
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) {
@@ -2581,7 +2590,7 @@ int moe_route_sort_sigmoid_table_probe(const uint16_t* bf16_bits, int n, float* 
   if (rc != MRS_OK) return rc;
   void* params[] = {&table, &bf16_bits, &n, &out_single, &out_pair};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(k_sigmoid_table_probe), dim3((n + 255) / 256),
-                                         dim3(256), params, kSigBytes, st);
+                                         dim3(256), params, kSigLdsBytes, st);
   return err == hipSuccess ? MRS_OK : MRS_ERR_LAUNCH;
 }
 

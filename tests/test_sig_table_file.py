@@ -24,8 +24,8 @@ def _table():
 def test_generated_table_equals_oracle():
     tab = _table()
     assert tab.size == 8192
-    t = np.arange(8192) >> 1
-    s = np.arange(8192) & 1
+    t = np.arange(8192) & 4095
+    s = np.arange(8192) >> 12
     h = (((0x3300 + t) & 0x7FFF) | (s << 15)).astype(np.uint16)
     ref = orc.sigmoid_f32(orc.bf16_bits_to_f32(h))
     bad = np.flatnonzero(tab.view(np.uint32) != ref.view(np.uint32))
@@ -41,5 +41,5 @@ def test_clamping_outside_the_table_is_exact():
     assert np.all(orc.sigmoid_f32(small) == np.float32(0.5))
     assert np.all(orc.sigmoid_f32(-small) == np.float32(0.5))
     big = orc.bf16_bits_to_f32(np.arange(0x4300 - 1, 0x7F80, dtype=np.uint16))
-    assert np.all(orc.sigmoid_f32(big) == tab[2 * 4095])
-    assert np.all(orc.sigmoid_f32(-big) == tab[2 * 4095 + 1])
+    assert np.all(orc.sigmoid_f32(big) == tab[4095])
+    assert np.all(orc.sigmoid_f32(-big) == tab[4096 + 4095])
