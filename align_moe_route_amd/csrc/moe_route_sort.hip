@@ -697,33 +697,49 @@ __device__ __forceinline__ uint32_t seg_bcast(uint32_t u) {
   const uint32_t lo = readlane(u, 31), hi = readlane(u, 63);
   return lane_id() < 32 ? lo : hi;
 }
+// The segment's maximum (minimum) in its last lane only (lane SEG - 1 of the
+// segment); for a value that only one lane reads afterwards.
 template <int SEG>
-__device__ __forceinline__ uint32_t seg_max_u32(uint32_t u) {
+__device__ __forceinline__ uint32_t seg_max_last(uint32_t u) {
   u = max(u, dpp<kRowShr1>(0u, u));
   u = max(u, dpp<kRowShr2>(0u, u));
   u = max(u, dpp<kRowShr4>(0u, u));
   u = max(u, dpp<kRowShr8>(0u, u));
   u = max(u, dpp<kRowBcast15, 0xA>(0u, u));
   if constexpr (SEG == 64) u = max(u, dpp<kRowBcast31, 0xC>(0u, u));
-  return seg_bcast<SEG>(u);
+  return u;
 }
 template <int SEG>
-__device__ __forceinline__ uint32_t seg_min_u32(uint32_t u) {
+__device__ __forceinline__ uint32_t seg_min_last(uint32_t u) {
   u = min(u, dpp<kRowShr1>(0xFFFFFFFFu, u));
   u = min(u, dpp<kRowShr2>(0xFFFFFFFFu, u));
   u = min(u, dpp<kRowShr4>(0xFFFFFFFFu, u));
   u = min(u, dpp<kRowShr8>(0xFFFFFFFFu, u));
   u = min(u, dpp<kRowBcast15, 0xA>(0xFFFFFFFFu, u));
   if constexpr (SEG == 64) u = min(u, dpp<kRowBcast31, 0xC>(0xFFFFFFFFu, u));
-  return seg_bcast<SEG>(u);
+  return u;
+}
+template <int SEG>
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t u) {
+  return seg_bcast<SEG>(seg_max_last<SEG>(u));
+}
+template <int SEG>
+__device__ __forceinline__ uint32_t seg_min_u32(uint32_t u) {
+  return seg_bcast<SEG>(seg_min_last<SEG>(u));
+}
+// Row shift with every row enabled: lanes shifted in from outside the row
+// read 0 (bound_ctrl), so the add can take the shifted operand directly.
+template <int CTRL>
+__device__ __forceinline__ uint32_t shr0(uint32_t u) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)u, CTRL, 0xF, 0xF, true);
 }
 template <int SEG>
 __device__ __forceinline__ int seg_incl_scan(int v) {
   uint32_t u = (uint32_t)v;
-  u += dpp<kRowShr1>(0u, u);
-  u += dpp<kRowShr2>(0u, u);
-  u += dpp<kRowShr4>(0u, u);
-  u += dpp<kRowShr8>(0u, u);
+  u += shr0<kRowShr1>(u);
+  u += shr0<kRowShr2>(u);
+  u += shr0<kRowShr4>(u);
+  u += shr0<kRowShr8>(u);
   u += dpp<kRowBcast15, 0xA>(0u, u);
   if constexpr (SEG == 64) u += dpp<kRowBcast31, 0xC>(0u, u);
   return (int)u;
@@ -735,10 +751,15 @@ __device__ __forceinline__ double seg_sum_d(double v) {
     const uint32_t lo = sh((uint32_t)b), hi = sh((uint32_t)(b >> 32));
     return x + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
   };
-  v = step(v, [](uint32_t u) { return dpp<kRowShr1>(0u, u); });
-  v = step(v, [](uint32_t u) { return dpp<kRowShr2>(0u, u); });
-  v = step(v, [](uint32_t u) { return dpp<kRowShr4>(0u, u); });
-  v = step(v, [](uint32_t u) { return dpp<kRowShr8>(0u, u); });
+  // row shifts with every row enabled: lanes shifted in from outside the row
+  // read 0 (bound_ctrl), so no zeroed destination is needed
+  auto shr = [](uint32_t u, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)u, decltype(ctrl)::value, 0xF, 0xF, true);
+  };
+  v = step(v, [&](uint32_t u) { return shr(u, std::integral_constant<int, kRowShr1>{}); });
+  v = step(v, [&](uint32_t u) { return shr(u, std::integral_constant<int, kRowShr2>{}); });
+  v = step(v, [&](uint32_t u) { return shr(u, std::integral_constant<int, kRowShr4>{}); });
+  v = step(v, [&](uint32_t u) { return shr(u, std::integral_constant<int, kRowShr8>{}); });
   v = step(v, [](uint32_t u) { return dpp<kRowBcast15, 0xA>(0u, u); });
   if constexpr (SEG == 64) v = step(v, [](uint32_t u) { return dpp<kRowBcast31, 0xC>(0u, u); });
   const uint64_t b = __double_as_longlong(v);
@@ -1024,18 +1045,19 @@ __device__ __forceinline__ int lean_token(const Args& a, const Lds& L, bool act,
   const uint32_t u1 = allowed ? f2s(lm) : 0u;
   const uint32_t u2 = (allowed && two) ? f2s(l2) : 0u;
   const unsigned long long ab = __ballot(allowed);
-  const uint32_t vmax = seg_max_u32<SEG>(u1);
-  const uint32_t vmin = seg_min_u32<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
+  // segment extremes, read from each segment's last lane
+  const uint32_t vmax = seg_max_last<SEG>(u1);
+  const uint32_t vmin = seg_min_last<SEG>(allowed ? (two ? u2 : u1) : 0xFFFFFFFFu);
   // lower end of the search: the smallest kept lane maximum when there are at
   // least k kept lanes (every lane maximum reaches it), else the smallest value
-  const uint32_t vmin1 = seg_min_u32<SEG>(allowed ? u1 : 0xFFFFFFFFu);
+  const uint32_t vmin1 = seg_min_last<SEG>(allowed ? u1 : 0xFFFFFFFFu);
   uint32_t Ts[NSEG], bs[NSEG];
   int okseg[NSEG];
 #pragma unroll
   for (int q = 0; q < NSEG; ++q) {
     const int nal = (int)__popcll(seg_bits<SEG>(ab, q));
-    const uint32_t hi = readlane(vmax, q * SEG);
-    const uint32_t lo = nal >= a.k ? readlane(vmin1, q * SEG) : readlane(vmin, q * SEG);
+    const uint32_t hi = readlane(vmax, q * SEG + SEG - 1);
+    const uint32_t lo = nal >= a.k ? readlane(vmin1, q * SEG + SEG - 1) : readlane(vmin, q * SEG + SEG - 1);
     const int nval = nal * (two ? 2 : 1);
     okseg[q] = nval >= a.k;
     const int top = (lo >= hi) ? -1 : 31 - __builtin_clz(hi ^ lo);
