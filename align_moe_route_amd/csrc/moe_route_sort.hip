@@ -102,6 +102,7 @@ struct Args {
   int M, E, k, n_group, topk_group, block;
   uint32_t blk_sh;        // n / block == (n * blk_mul) >> blk_sh for 0 <= n < 2^31
   unsigned long long blk_mul;
+  uint32_t k_mul;         // q / k == (q * k_mul) >> 18 for 0 <= q < 4096
   int G;       // experts per group
   int seg;    // lanes per token in the wave path (32 or 64)
   int lg_lpg;  // log2 of the lanes per group in the wave path (seg / n_group)
@@ -258,6 +259,10 @@ __device__ __forceinline__ float next_down(float f) {
 __device__ __forceinline__ int div_block(int n, const Args& a) {
   return (int)(((unsigned long long)(uint32_t)n * a.blk_mul) >> a.blk_sh);
 }
+// q / k for a slot index q of at most kTwMax tokens (q < 4096, k <= 64):
+// k_mul = ceil(2^18 / k) = (2^18 + e) / k with e < k adds q*e/(k*2^18) to
+// q/k, less than 1/k because q*(k-1) < 2^18, so the floor is exact.
+__device__ __forceinline__ int div_k(int q, const Args& a) { return (int)(((uint32_t)q * a.k_mul) >> 18); }
 __device__ __forceinline__ int pad_block(int c, const Args& a) {
   return (c == 0) ? 0 : (div_block(c - 1, a) + 1) * a.block;
 }
@@ -611,7 +616,9 @@ struct Ownership {
     const int j = ls & (w - 1);
     e_slot0 = (ls - j) * epl + 4 * j;
   }
-  __device__ __forceinline__ int expert(int i) const { return e_slot0 + 4 * w * (i >> 2) + (i & 3); }
+  __device__ __forceinline__ int expert(int i) const {
+    return w == 1 ? e_slot0 + i : e_slot0 + 4 * w * (i >> 2) + (i & 3);  // w is a constant 1 but for FP32 vectors
+  }
   // slot and lane of expert e: the inverse of expert()
   __device__ static void place(int e, int epl, int w, int& slot, int& lane) {
     const int r = e % (w * epl), v = r >> 2;
@@ -1540,7 +1547,7 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
     for (int q = tid; q < sentinel; q += kWave) {
       const int e = L.ids[q] - a.e_lo;
       if ((unsigned)e < (unsigned)a.EL)
-        a.sorted_ids[L.off[e] + __popcll(bits[e] & ((1ull << (q / a.k)) - 1ull))] = q;
+        a.sorted_ids[L.off[e] + __popcll(bits[e] & ((1ull << div_k(q, a)) - 1ull))] = q;
     }
     return;
   }
@@ -1548,7 +1555,7 @@ __global__ __launch_bounds__(kWG) void k_small(Args a) {
   if (tid == 0) *a.npp = total;
   write_padding(a, a.EL, L.off, [&](int e) { return __popcll(bits[e]); });
   for (int q = tid; q < sentinel; q += kWG) {
-    const int tl = q / a.k;
+    const int tl = div_k(q, a);
     const int e = L.ids[q] - a.e_lo;
     if ((unsigned)e < (unsigned)a.EL) {
       const int rank = __popcll(bits[e] & ((1ull << tl) - 1ull));
@@ -1574,7 +1581,7 @@ __global__ __launch_bounds__(kWG) void k_select(Args a) {
   const int ns = nt * a.k;
   int32_t* rec = a.ws_slot + (size_t)t0 * a.k;
   for (int q = threadIdx.x; q < ns; q += kWG) {
-    const int tl = q / a.k;
+    const int tl = div_k(q, a);
     const int e = L.ids[q] - a.e_lo;
     rec[q] = (unsigned)e < (unsigned)a.EL ? (e | (__popcll(bits[e] & ((1ull << tl) - 1ull)) << 16)) : -1;
   }
@@ -1851,7 +1858,7 @@ __device__ void ids_local(const Args& a, const IdsLds& L, int t0, int nt) {
     const int q = tid + j * kWG;
     const int e = iv[j];
     if (q < ns && e >= 0 && e < a.E) {
-      const unsigned long long bit = 1ull << (q / a.k);
+      const unsigned long long bit = 1ull << div_k(q, a);
       if (atomicOr(&L.bits[e], bit) & bit) L.misc[0] = 1;  // this token already routes to e
     }
   }
@@ -1863,7 +1870,7 @@ __device__ void ids_local(const Args& a, const IdsLds& L, int t0, int nt) {
       const int q = tid + j * kWG;
       const int e = iv[j];
       if (q < ns) {
-        const int tl = q / a.k;
+        const int tl = div_k(q, a);
         L.rec[q] = (e >= 0 && e < a.E) ? (e | (__popcll(L.bits[e] & ((1ull << tl) - 1ull)) << 16)) : -1;
       }
     }
@@ -2333,6 +2340,7 @@ static int route_sort_impl(const void* logits, const float* bias, int M, int E, 
     a.blk_sh = 31 + l;
     a.blk_mul = ((1ull << (31 + l)) + (unsigned long long)block - 1) / (unsigned long long)block;
   }
+  a.k_mul = ((1u << 18) + (uint32_t)k - 1u) / (uint32_t)k;
   a.G = E / n_group;
   a.gstage = (n_group > 1 && topk_group < n_group && a.G > 1) ? 1 : 0;
   a.out_ids = out_ids;
@@ -2547,6 +2555,7 @@ static int sort_from_ids_impl(const int32_t* ids, int M, int E, int k, int block
     a.blk_sh = 31 + l;
     a.blk_mul = ((1ull << (31 + l)) + (unsigned long long)block - 1) / (unsigned long long)block;
   }
+  a.k_mul = ((1u << 18) + (uint32_t)k - 1u) / (uint32_t)k;
   a.in_ids = ids;
   a.sorted_ids = sorted_ids;
   a.eob = expert_of_block;
